@@ -1,0 +1,11 @@
+"""MI355X-native paged KV cache: slot-mapping scatter and paged decode read.
+
+The compute lives in ``libpkv.so`` (hand-written HIP kernels for gfx950 behind a
+C ABI declared in ``include/pkv.h``); this package is a thin ctypes binding that
+marshals torch tensors into pointers and a HIP stream.  The library is loaded
+on first use, and a missing library is an error: there is no fallback path.
+"""
+from .binding import (  # noqa: F401
+    PkvError, reshape_and_cache, paged_attention, paged_attention_into,
+    workspace_size, library_path, load_library,
+)

@@ -1,0 +1,179 @@
+"""ctypes binding of libpkv.so (see include/pkv.h for the contract).
+
+Argument marshalling only: shapes, dtypes and devices of torch tensors are
+read on the host, raw device pointers and the current HIP stream are passed
+to the C ABI, and a non-zero status becomes a ``PkvError``.  Every step of the
+scatter and the read runs in the library's kernels.  PyTorch provides device
+memory (including the read's workspace) and streams, nothing else.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libpkv.so")
+
+PKV_F32 = 0
+PKV_BF16 = 1
+_DTYPES = {torch.float32: PKV_F32, torch.bfloat16: PKV_BF16}
+
+_lib = None
+
+
+class PkvError(RuntimeError):
+    """A libpkv call returned a non-zero status."""
+
+    def __init__(self, status: int, message: str):
+        super().__init__("libpkv status %d: %s" % (status, message))
+        self.status = status
+
+
+class AttnDesc(ctypes.Structure):
+    _fields_ = [("rows", ctypes.c_int32), ("n_heads", ctypes.c_int32),
+                ("n_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("block_size", ctypes.c_int32), ("max_blocks_per_row", ctypes.c_int32),
+                ("num_blocks", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("out_dtype", ctypes.c_int32), ("partition_tokens", ctypes.c_int32)]
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def load_library():
+    """Load libpkv.so once.  A missing library is an error, never a fallback."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise ImportError("libpkv.so is not built (expected at %s); run "
+                          "`python -c 'import __graft_entry__ as g; g.build()'`" % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, i32, i64, sz = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
+    lib.pkv_reshape_and_cache.argtypes = [vp, vp, vp, i64, vp, vp, i64, i32, i32, i32, i32, vp]
+    lib.pkv_reshape_and_cache.restype = ctypes.c_int
+    lib.pkv_paged_attention.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp,
+                                        ctypes.c_float, vp, vp, sz, vp]
+    lib.pkv_paged_attention.restype = ctypes.c_int
+    lib.pkv_paged_attention_workspace_size.argtypes = [ctypes.POINTER(AttnDesc)]
+    lib.pkv_paged_attention_workspace_size.restype = sz
+    lib.pkv_strerror.argtypes = [ctypes.c_int]
+    lib.pkv_strerror.restype = ctypes.c_char_p
+    lib.pkv_version.argtypes = []
+    lib.pkv_version.restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        msg = load_library().pkv_strerror(status).decode()
+        raise PkvError(status, msg)
+
+
+def _dtype_code(t: torch.Tensor) -> int:
+    try:
+        return _DTYPES[t.dtype]
+    except KeyError:
+        raise TypeError("unsupported dtype %s (float32 or bfloat16)" % t.dtype) from None
+
+
+def _require(cond: bool, msg: str):
+    if not cond:
+        raise ValueError(msg)
+
+
+def _on_gpu(*ts):
+    dev = ts[0].device
+    for t in ts:
+        _require(t.is_cuda, "every tensor must live on the GPU")
+        _require(t.device == dev, "every tensor must live on the same GPU")
+        _require(t.is_contiguous(), "every tensor must be contiguous")
+    return dev
+
+
+def _stream_handle(device) -> int:
+    return torch.cuda.current_stream(device).cuda_stream
+
+
+def reshape_and_cache(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
+                      k_pool: torch.Tensor, v_pool: torch.Tensor) -> None:
+    """Scatter k, v [T, n_kv, hd] into k_pool, v_pool [nb, n_kv, bs, hd] at
+    slot_mapping [T] (int64; negative = skip), on the current stream."""
+    dev = _on_gpu(k, v, slot_mapping, k_pool, v_pool)
+    _require(k.dim() == 3 and v.shape == k.shape, "k, v must be [T, n_kv_heads, head_dim]")
+    _require(k_pool.dim() == 4 and v_pool.shape == k_pool.shape,
+             "pools must be [num_blocks, n_kv_heads, block_size, head_dim]")
+    _require(k_pool.shape[1] == k.shape[1] and k_pool.shape[3] == k.shape[2],
+             "pools and k/v disagree on n_kv_heads or head_dim")
+    _require(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (k.shape[0],),
+             "slot_mapping must be int64 [T]")
+    dt = _dtype_code(k)
+    _require(v.dtype == k.dtype and k_pool.dtype == k.dtype and v_pool.dtype == k.dtype,
+             "k, v and pools must share one dtype")
+    nb, nkv, bs, hd = k_pool.shape
+    _check(load_library().pkv_reshape_and_cache(
+        k.data_ptr(), v.data_ptr(), slot_mapping.data_ptr(), k.shape[0],
+        k_pool.data_ptr(), v_pool.data_ptr(), nb, bs, nkv, hd, dt, _stream_handle(dev)))
+
+
+def _desc(q, k_pool, block_table, out_dtype, partition_tokens) -> AttnDesc:
+    rows, n_heads, hd = q.shape
+    nb, nkv, bs, hd2 = k_pool.shape
+    _require(hd == hd2, "q and pools disagree on head_dim")
+    return AttnDesc(rows=rows, n_heads=n_heads, n_kv_heads=nkv, head_dim=hd, block_size=bs,
+                    max_blocks_per_row=block_table.shape[1], num_blocks=nb,
+                    dtype=_dtype_code(q), out_dtype=out_dtype,
+                    partition_tokens=int(partition_tokens))
+
+
+def workspace_size(q: torch.Tensor, k_pool: torch.Tensor, block_table: torch.Tensor,
+                   out_dtype: Optional[torch.dtype] = None, partition_tokens: int = 0) -> int:
+    od = _DTYPES[out_dtype or q.dtype]
+    d = _desc(q, k_pool, block_table, od, partition_tokens)
+    return int(load_library().pkv_paged_attention_workspace_size(ctypes.byref(d)))
+
+
+def paged_attention_into(q, k_pool, v_pool, block_table, context_lens, scale, out,
+                         workspace: Optional[torch.Tensor] = None,
+                         partition_tokens: int = 0) -> torch.Tensor:
+    """Paged decode read into a caller-provided `out` [rows, n_heads, hd]
+    (float32 or bfloat16).  `workspace` is a uint8 GPU tensor; when None one of
+    the required size is allocated by torch for this call."""
+    dev = _on_gpu(q, k_pool, v_pool, block_table, context_lens, out)
+    _require(q.dim() == 3, "q must be [rows, n_heads, head_dim]")
+    _require(k_pool.dim() == 4 and v_pool.shape == k_pool.shape,
+             "pools must be [num_blocks, n_kv_heads, block_size, head_dim]")
+    _require(k_pool.dtype == q.dtype and v_pool.dtype == q.dtype, "q and pools must share one dtype")
+    _require(block_table.dtype == torch.int32 and block_table.dim() == 2
+             and block_table.shape[0] == q.shape[0], "block_table must be int32 [rows, max_blocks]")
+    _require(context_lens.dtype == torch.int32 and context_lens.shape == (q.shape[0],),
+             "context_lens must be int32 [rows]")
+    _require(out.shape == q.shape, "out must be [rows, n_heads, head_dim]")
+    d = _desc(q, k_pool, block_table, _dtype_code(out), partition_tokens)
+    lib = load_library()
+    need = int(lib.pkv_paged_attention_workspace_size(ctypes.byref(d)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _on_gpu(workspace)
+    _check(lib.pkv_paged_attention(
+        ctypes.byref(d), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
+        block_table.data_ptr(), context_lens.data_ptr(), ctypes.c_float(scale), out.data_ptr(),
+        workspace.data_ptr() if need else None, workspace.numel() * workspace.element_size(),
+        _stream_handle(dev)))
+    return out
+
+
+def paged_attention(q, k_pool, v_pool, block_table, context_lens, scale, out=None,
+                    partition_tokens: int = 0) -> torch.Tensor:
+    """nanoserve-style call: returns attention output [rows, n_heads, head_dim]
+    in q's dtype (or writes `out` if given)."""
+    if out is None:
+        out = torch.empty_like(q)
+    return paged_attention_into(q, k_pool, v_pool, block_table, context_lens, scale, out,
+                                partition_tokens=partition_tokens)
