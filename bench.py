@@ -1,0 +1,204 @@
+#!/usr/bin/env python3
+"""Benchmark of one decode step of the paged KV cache on one MI355X.
+
+A step is the whole hot path over one batch: the slot-mapping scatter of each
+row's new token K/V into the pool, then the paged decode read of every row
+(GQA heads, split-context partitions + merge).  The workload is a
+Llama-3-8B-shaped attention layer: 64 rows, 32 query heads, 8 kv heads,
+head_dim 128, bf16 pool of 16-position blocks, context lengths uniform in
+[512, 4096], block tables drawn from a 1.5x pool.  Every input is synthetic
+and seeded; inputs are resident in HBM before timing starts.
+
+Prints one JSON line: whole-step HBM throughput (algorithmic bytes / step
+time), the read's µs per call and its fraction of MI355X's 8 TB/s, the read
+kernel timed with HIP events on the stream it runs on, and the CPU oracle
+timed on this host as a reported baseline.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "paged decode read µs/call + achieved HBM GB/s (% peak), 8B-shaped layer"
+HBM_PEAK_GBS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=200)
+    ap.add_argument("--warmup", type=int, default=20)
+    ap.add_argument("--workload", default="llama3_8b_layer")
+    ap.add_argument("--partition", type=int, default=0, help="partition_tokens (0 = library default)")
+    ap.add_argument("--flushed", type=int, default=30,
+                    help="extra reads timed with the 256 MB Infinity Cache flushed before each")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0,
+                    help="target CPU time of the oracle baseline (0 disables it)")
+    return ap.parse_args()
+
+
+def cpu_baseline(batch, new_k, new_v, slots_h, budget_s):
+    """The CPU oracle (plain C, one thread) on the same inputs, copied to host
+    memory outside the timing: scatter of the step's new tokens, then the read
+    of every row.  Repeated until about `budget_s` seconds of CPU work."""
+    import oracle
+    from paged_kv_cache_13_amd import harness
+
+    oracle.build()
+    q = batch.q.cpu()
+    kp = batch.k_pool.cpu()
+    vp = batch.v_pool.cpu()
+    kn, vn = new_k.cpu(), new_v.cpu()
+    cfg = batch.cfg
+    reps, spent = 0, 0.0
+    while spent < budget_s and (reps == 0 or spent / reps * (reps + 1) <= 2 * budget_s):
+        t0 = time.perf_counter()
+        oracle.reshape_and_cache(kn, vn, slots_h, kp, vp)
+        oracle.paged_attention(q, kp, vp, batch.table_host, batch.ctx_host, batch.scale)
+        spent += time.perf_counter() - t0
+        reps += 1
+    nbytes = harness.read_bytes(batch.ctx_host, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim,
+                                cfg.block_size, 2, 2)
+    nbytes += harness.scatter_bytes(cfg.rows, cfg.n_kv_heads, cfg.head_dim, 2)
+    per = spent / reps
+    return {"value": round(nbytes / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "ms_per_step": round(per * 1e3, 2),
+            "sample": "the full workload (%d rows, sum ctx %d), %d step(s): scatter + read, "
+                      "single-threaded C in fp64" % (cfg.rows, int(batch.ctx_host.sum()), reps),
+            "cpu": cpu_model()}
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py measures one GPU only: this build has no multi-GPU path "
+              "(--gpus %d requested)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_13_amd as pkv
+    from paged_kv_cache_13_amd import harness, synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    pkv.load_library()
+    cfg = synth.CONFIGS[args.workload]
+    batch = synth.make_batch(cfg, device=dev)
+    bs = cfg.block_size
+    elem = 2 if cfg.dtype == "bf16" else 4
+
+    # The step's new token of each row is its last position (already counted in
+    # context_lens): its slot is overwritten every step, so every step reads the
+    # same lengths.
+    last = batch.ctx_host - 1
+    slots_h = (batch.table_host[np.arange(cfg.rows), last // bs].astype(np.int64) * bs + last % bs)
+    slots = torch.from_numpy(slots_h).to(dev)
+    g = torch.Generator(device=dev).manual_seed(cfg.seed + 100)
+    new_k = torch.randn(cfg.rows, cfg.n_kv_heads, cfg.head_dim, generator=g, device=dev).to(batch.q.dtype)
+    new_v = torch.randn(cfg.rows, cfg.n_kv_heads, cfg.head_dim, generator=g, device=dev).to(batch.q.dtype)
+    out = torch.empty_like(batch.q)
+    wsz = pkv.workspace_size(batch.q, batch.k_pool, batch.block_table, partition_tokens=args.partition)
+    ws = torch.empty(max(wsz, 1), dtype=torch.uint8, device=dev)
+
+    def scatter():
+        pkv.reshape_and_cache(new_k, new_v, slots, batch.k_pool, batch.v_pool)
+
+    def read():
+        pkv.paged_attention_into(batch.q, batch.k_pool, batch.v_pool, batch.block_table,
+                                 batch.context_lens, batch.scale, out, ws,
+                                 partition_tokens=args.partition)
+
+    stream = torch.cuda.current_stream(dev)
+    for _ in range(args.warmup):
+        scatter()
+        read()
+    torch.cuda.synchronize()
+
+    K = args.steps
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(K):
+        scatter()
+        ev[i][0].record(stream)
+        read()
+        ev[i][1].record(stream)
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    read_ms = np.array([a.elapsed_time(b) for a, b in ev])
+
+    # reads with the Infinity Cache flushed (a 512 MiB write) before each
+    flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
+    fl_ms = []
+    for _ in range(args.flushed):
+        flush.fill_(1)
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        read()
+        b.record(stream)
+        torch.cuda.synchronize()
+        fl_ms.append(a.elapsed_time(b))
+    del flush
+
+    rb = harness.read_bytes(batch.ctx_host, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, bs, elem, elem)
+    sb = harness.scatter_bytes(cfg.rows, cfg.n_kv_heads, cfg.head_dim, elem)
+    ms_step = wall * 1e3 / K
+    read_us = float(read_ms.mean() * 1e3)
+    achieved = rb / (read_us * 1e-6) / 1e9
+    stats = harness.ReadStats("streamed", block=bs)
+    stats.record(cfg.rows, cfg.n_heads, 1, int(batch.ctx_host.max()))
+    print("readstats: mode=%s block=%d calls=%d rows=%d score_cells=%d held_cells=%d saving=%.1fx"
+          % (stats.mode, stats.block, stats.calls, stats.rows, stats.score_cells, stats.held_cells,
+             stats.saving), file=sys.stderr)
+
+    res = {
+        "metric": METRIC,
+        "value": round((rb + sb) / (ms_step * 1e-3) / 1e9, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cfg.dtype,
+        "data": "synthetic",
+        "config": {"workload": cfg.name, "rows": cfg.rows, "n_heads": cfg.n_heads,
+                   "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim, "block_size": bs,
+                   "context_lens": "uniform[512,4096]" if cfg.name == "llama3_8b_layer" else str(cfg.ctx),
+                   "sum_ctx": int(batch.ctx_host.sum()), "num_blocks": batch.num_blocks,
+                   "partition_tokens": args.partition or 512},
+        "read_us": round(read_us, 2),
+        "read_us_median": round(float(np.median(read_ms)) * 1e3, 2),
+        "read_us_flushed": round(float(np.median(fl_ms)) * 1e3, 2) if fl_ms else None,
+        "read_pct_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
+        "read_bytes": rb,
+        "scatter_bytes": sb,
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
+                     "kernel": "paged decode read (decode_partition + decode_merge)"},
+    }
+    if args.cpu_seconds > 0:
+        res["cpu_baseline"] = cpu_baseline(batch, new_k, new_v, slots_h, args.cpu_seconds)
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,163 @@
+// C ABI of libpkv.so (declared and documented in include/pkv.h).
+//
+// Every entry point validates its arguments on the host and returns a status
+// before touching the HIP runtime, so a refused call enqueues nothing.  Launch
+// geometry comes from host shapes only (max_blocks_per_row, never the device
+// lengths): nanoserve "Day 60" page, "Why it matters" -- reading lengths back
+// would be a device sync on every call.
+#include <limits.h>
+
+#include "pkv.h"
+#include "pkv_internal.h"
+
+namespace {
+
+constexpr int32_t kDefaultPartition = 512;
+constexpr int32_t kMaxGroup = 16;
+constexpr int32_t kMaxPartitionBlocks = 4096;  // LDS holds one partition's block ids (16 KB)
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
+bool dtype_ok(int32_t d) { return d == PKV_F32 || d == PKV_BF16; }
+bool head_dim_ok(int32_t h) { return h == 16 || h == 64 || h == 128; }
+bool block_size_ok(int32_t b) { return b == 8 || b == 16 || b == 32; }
+int64_t elem_bytes(int32_t d) { return d == PKV_F32 ? 4 : 2; }
+int32_t log2i(int32_t x) {
+  int32_t l = 0;
+  while ((1 << l) < x) ++l;
+  return l;
+}
+
+// Pool bytes fit in int64 and in the addressable range.
+bool pool_fits(int64_t num_blocks, int32_t bs, int32_t n_kv, int32_t hd, int32_t dtype) {
+  const int64_t per_block = (int64_t)bs * n_kv * hd * elem_bytes(dtype);
+  return num_blocks >= 1 && num_blocks <= INT64_MAX / per_block;
+}
+
+struct Plan {
+  int32_t group, partition, max_parts, log2_bs;
+  size_t ws_bytes;
+};
+
+int plan_decode(const pkv_attn_desc *d, Plan *pl) {
+  if (!d) return PKV_ERR_NULL;
+  if (!dtype_ok(d->dtype) || !dtype_ok(d->out_dtype)) return PKV_ERR_DTYPE;
+  if (d->rows < 0 || d->rows > 65535) return PKV_ERR_SHAPE;
+  if (d->n_heads < 1 || d->n_kv_heads < 1 || d->n_kv_heads > 65535) return PKV_ERR_HEADS;
+  if (d->n_heads % d->n_kv_heads != 0 || d->n_heads / d->n_kv_heads > kMaxGroup) return PKV_ERR_HEADS;
+  if (!head_dim_ok(d->head_dim)) return PKV_ERR_HEAD_DIM;
+  if (!block_size_ok(d->block_size)) return PKV_ERR_BLOCK_SIZE;
+  if (d->max_blocks_per_row < 1 || (int64_t)d->max_blocks_per_row * d->block_size > INT_MAX)
+    return PKV_ERR_SHAPE;
+  if (d->num_blocks > INT_MAX ||
+      !pool_fits(d->num_blocks, d->block_size, d->n_kv_heads, d->head_dim, d->dtype))
+    return PKV_ERR_SHAPE;
+  const int32_t cap = d->max_blocks_per_row * d->block_size;
+  int32_t part = d->partition_tokens;
+  if (part == 0) part = kDefaultPartition;
+  if (part < 0 || part % d->block_size != 0) return PKV_ERR_PARTITION;
+  if (part > cap) part = cap;  // one partition covers every row: no split
+  if (part / d->block_size > kMaxPartitionBlocks) return PKV_ERR_PARTITION;
+  pl->group = d->n_heads / d->n_kv_heads;
+  pl->partition = part;
+  pl->max_parts = (cap + part - 1) / part;
+  pl->log2_bs = log2i(d->block_size);
+  pl->ws_bytes = 0;
+  if (pl->max_parts > 1 && d->rows > 0)
+    pl->ws_bytes =
+        pkv::ws_layout(d->rows, d->n_heads, pl->max_parts, d->head_dim).total_floats * sizeof(float);
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_version(void) { return 100; }
+
+const char *pkv_strerror(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "a required pointer is NULL";
+    case PKV_ERR_ALIGN: return "a buffer is not aligned (16 bytes for K/V/q/out/workspace)";
+    case PKV_ERR_DTYPE: return "unsupported dtype (0 = f32, 1 = bf16)";
+    case PKV_ERR_HEADS: return "n_heads must be a multiple of n_kv_heads with group <= 16";
+    case PKV_ERR_HEAD_DIM: return "head_dim must be 16, 64 or 128";
+    case PKV_ERR_BLOCK_SIZE: return "block_size must be 8, 16 or 32";
+    case PKV_ERR_SHAPE: return "a size is out of range or overflows";
+    case PKV_ERR_WORKSPACE: return "workspace missing or smaller than pkv_paged_attention_workspace_size";
+    case PKV_ERR_PARTITION: return "partition_tokens must be a positive multiple of block_size";
+    case PKV_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
+    default: return "unknown status";
+  }
+}
+
+int pkv_reshape_and_cache(const void *k, const void *v, const int64_t *slot_mapping,
+                          int64_t num_tokens, void *k_pool, void *v_pool, int64_t num_blocks,
+                          int32_t block_size, int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
+                          void *stream) {
+  if (!k || !v || !slot_mapping || !k_pool || !v_pool) return PKV_ERR_NULL;
+  if (!dtype_ok(dtype)) return PKV_ERR_DTYPE;
+  if (!head_dim_ok(head_dim)) return PKV_ERR_HEAD_DIM;
+  if (!block_size_ok(block_size)) return PKV_ERR_BLOCK_SIZE;
+  if (num_tokens < 0 || num_tokens > INT_MAX || n_kv_heads < 1 || n_kv_heads > 4096)
+    return PKV_ERR_SHAPE;
+  if (!pool_fits(num_blocks, block_size, n_kv_heads, head_dim, dtype)) return PKV_ERR_SHAPE;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(slot_mapping, 8))
+    return PKV_ERR_ALIGN;
+  if (num_tokens == 0) return PKV_OK;
+  const hipError_t e = pkv::launch_scatter(k, v, slot_mapping, num_tokens, k_pool, v_pool,
+                                           num_blocks, block_size, n_kv_heads, head_dim, dtype,
+                                           static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+size_t pkv_paged_attention_workspace_size(const pkv_attn_desc *d) {
+  Plan pl;
+  if (plan_decode(d, &pl) != PKV_OK) return 0;
+  return pl.ws_bytes;
+}
+
+int pkv_paged_attention(const pkv_attn_desc *d, const void *q, const void *k_pool,
+                        const void *v_pool, const int32_t *block_table,
+                        const int32_t *context_lens, float scale, void *out, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+  Plan pl;
+  const int st = plan_decode(d, &pl);
+  if (st != PKV_OK) return st;
+  if (!q || !k_pool || !v_pool || !block_table || !context_lens || !out) return PKV_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16) ||
+      !aligned(block_table, 4) || !aligned(context_lens, 4))
+    return PKV_ERR_ALIGN;
+  if (pl.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < pl.ws_bytes) return PKV_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return PKV_ERR_ALIGN;
+  }
+  if (d->rows == 0) return PKV_OK;
+  pkv::DecodeArgs a;
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.out = out;
+  a.ws = pl.ws_bytes ? static_cast<float *>(workspace) : nullptr;
+  a.rows = d->rows;
+  a.n_heads = d->n_heads;
+  a.n_kv_heads = d->n_kv_heads;
+  a.group = pl.group;
+  a.head_dim = d->head_dim;
+  a.block_size = d->block_size;
+  a.log2_bs = pl.log2_bs;
+  a.max_blocks_per_row = d->max_blocks_per_row;
+  a.partition_tokens = pl.partition;
+  a.max_parts = pl.max_parts;
+  a.num_blocks = d->num_blocks;
+  a.dtype = d->dtype;
+  a.out_dtype = d->out_dtype;
+  a.scale = scale;
+  const hipError_t e = pkv::launch_decode(a, static_cast<hipStream_t>(stream));
+  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+}  // extern "C"

@@ -1,0 +1,62 @@
+"""Helpers for GPU-vs-oracle parity tests (not collected by pytest)."""
+import numpy as np
+import torch
+
+import oracle
+import paged_kv_cache_13_amd as pkv
+
+DEV = "cuda:0"
+
+# nanoserve "Day 25" page, "What I learned", item 2: the kernel is held to the
+# reference at atol 1e-5, rtol 1e-4 (fp32).  bf16 output: atol 2e-2 (stated
+# for bf16 storage with fp32 accumulation); rtol kept at 1e-4.
+TOL = {torch.float32: dict(atol=1e-5, rtol=1e-4), torch.bfloat16: dict(atol=2e-2, rtol=1e-4)}
+
+
+def assert_close(got, ref, atol, rtol, what=""):
+    got = np.asarray(got, dtype=np.float64)
+    ref = np.asarray(ref, dtype=np.float64)
+    assert got.shape == ref.shape, (got.shape, ref.shape)
+    assert np.isfinite(got).all(), "%s: non-finite output at %s" % (what, np.argwhere(~np.isfinite(got))[:5])
+    diff = np.abs(got - ref)
+    bad = diff > atol + rtol * np.abs(ref)
+    if bad.any():
+        idx = np.argwhere(bad)[:5]
+        raise AssertionError("%s: %d/%d elements outside atol=%g rtol=%g; max |diff| %.3g; first %s"
+                             % (what, bad.sum(), bad.size, atol, rtol, diff.max(), idx.tolist()))
+
+
+def gpu_read(batch, out_dtype=None, partition=0):
+    out = torch.empty(batch.q.shape, dtype=out_dtype or batch.q.dtype, device=batch.q.device)
+    out.fill_(float("nan"))
+    pkv.paged_attention_into(batch.q, batch.k_pool, batch.v_pool, batch.block_table,
+                             batch.context_lens, batch.scale, out, partition_tokens=partition)
+    torch.cuda.synchronize()
+    return out
+
+
+def host_rows(batch, rows):
+    """Host copies of q and a compact pool holding only `rows`' blocks, with the
+    block table renumbered into it (paging invariance: the oracle's result does
+    not depend on where the blocks live)."""
+    rows = np.asarray(rows)
+    bs = batch.cfg.block_size
+    ids, table = [], np.zeros((len(rows), batch.table_host.shape[1]), dtype=np.int32)
+    for i, r in enumerate(rows):
+        need = -(-int(batch.ctx_host[r]) // bs)
+        table[i, :need] = np.arange(len(ids), len(ids) + need)
+        ids.extend(int(b) for b in batch.table_host[r, :need])
+    if not ids:
+        ids = [0]
+    idx = torch.tensor(ids, dtype=torch.long, device=batch.k_pool.device)
+    kp = batch.k_pool.index_select(0, idx).cpu()
+    vp = batch.v_pool.index_select(0, idx).cpu()
+    q = batch.q[torch.as_tensor(rows, device=batch.q.device)].cpu()
+    return q, kp, vp, table, batch.ctx_host[rows].copy()
+
+
+def oracle_read(batch, rows=None):
+    if rows is None:
+        rows = np.arange(batch.cfg.rows)
+    q, kp, vp, table, lens = host_rows(batch, rows)
+    return oracle.paged_attention(q, kp, vp, table, lens, batch.scale)
