@@ -19,8 +19,12 @@
  *     read must not read device values back on the host (no sync).
  *
  * Layout (all buffers device memory, row-major, contiguous, 16-byte aligned):
- *   k_pool, v_pool : [num_blocks, n_kv_heads, block_size, head_dim]
- *                    (each (block, kv head) tile is one contiguous run)
+ *   k_pool         : [num_blocks, n_kv_heads, block_size, head_dim]
+ *   v_pool         : [num_blocks, n_kv_heads, head_dim, block_size]
+ *                    (each (block, kv head) tile is one contiguous run; inside
+ *                    it K is position-major and V dimension-major, so both
+ *                    contractions of the read find their reduction index
+ *                    contiguous: head_dim for q.K, positions for p.V)
  *   q, out         : [rows, n_heads, head_dim]
  *   k, v (scatter) : [num_tokens, n_kv_heads, head_dim]
  *   slot_mapping   : [num_tokens] int64; slot s = block * block_size + offset
@@ -92,12 +96,14 @@ typedef struct pkv_attn_desc {
  * ("Day 25" page, "What I learned", item 1: scatter and gather are exact.)
  *
  * For each token t with s = slot_mapping[t] >= 0: for every kv head g,
- * k_pool[s / block_size, g, s % block_size, :] = k[t, g, :] and the same for
- * v, copied bit for bit.  Tokens with a negative slot are skipped (padding).
+ * k_pool[s / block_size, g, s % block_size, :] = k[t, g, :] and
+ * v_pool[s / block_size, g, :, s % block_size] = v[t, g, :], copied bit for
+ * bit.  Tokens with a negative slot are skipped (padding).
  *
  *   k, v          device [num_tokens, n_kv_heads, head_dim] of `dtype`
  *   slot_mapping  device [num_tokens] int64
- *   k_pool, v_pool device [num_blocks, n_kv_heads, block_size, head_dim]
+ *   k_pool        device [num_blocks, n_kv_heads, block_size, head_dim]
+ *   v_pool        device [num_blocks, n_kv_heads, head_dim, block_size]
  *   num_tokens >= 0 (0 enqueues nothing); num_blocks >= 1
  * Caller contract (not checked on device): slots < num_blocks * block_size
  * (larger ones are skipped) and distinct within one call (duplicates race).
@@ -123,7 +129,8 @@ int pkv_reshape_and_cache(const void *k, const void *v, const int64_t *slot_mapp
  *
  *   d             shapes and dtypes (host struct, read during the call only)
  *   q             device [rows, n_heads, head_dim] of d->dtype
- *   k_pool,v_pool device [num_blocks, n_kv_heads, block_size, head_dim]
+ *   k_pool        device [num_blocks, n_kv_heads, block_size, head_dim]
+ *   v_pool        device [num_blocks, n_kv_heads, head_dim, block_size]
  *   block_table   device [rows, max_blocks_per_row] int32
  *   context_lens  device [rows] int32
  *   scale         softmax scale applied to the fp32 dot product

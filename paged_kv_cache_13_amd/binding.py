@@ -96,18 +96,25 @@ def _on_gpu(*ts):
     return dev
 
 
+def _check_pools(k_pool, v_pool):
+    _require(k_pool.dim() == 4, "k_pool must be [num_blocks, n_kv_heads, block_size, head_dim]")
+    nb, nkv, bs, hd = k_pool.shape
+    _require(tuple(v_pool.shape) == (nb, nkv, hd, bs),
+             "v_pool must be [num_blocks, n_kv_heads, head_dim, block_size]")
+
+
 def _stream_handle(device) -> int:
     return torch.cuda.current_stream(device).cuda_stream
 
 
 def reshape_and_cache(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
                       k_pool: torch.Tensor, v_pool: torch.Tensor) -> None:
-    """Scatter k, v [T, n_kv, hd] into k_pool, v_pool [nb, n_kv, bs, hd] at
-    slot_mapping [T] (int64; negative = skip), on the current stream."""
+    """Scatter k, v [T, n_kv, hd] into k_pool [nb, n_kv, bs, hd] and v_pool
+    [nb, n_kv, hd, bs] at slot_mapping [T] (int64; negative = skip), on the
+    current stream."""
     dev = _on_gpu(k, v, slot_mapping, k_pool, v_pool)
     _require(k.dim() == 3 and v.shape == k.shape, "k, v must be [T, n_kv_heads, head_dim]")
-    _require(k_pool.dim() == 4 and v_pool.shape == k_pool.shape,
-             "pools must be [num_blocks, n_kv_heads, block_size, head_dim]")
+    _check_pools(k_pool, v_pool)
     _require(k_pool.shape[1] == k.shape[1] and k_pool.shape[3] == k.shape[2],
              "pools and k/v disagree on n_kv_heads or head_dim")
     _require(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (k.shape[0],),
@@ -146,8 +153,7 @@ def paged_attention_into(q, k_pool, v_pool, block_table, context_lens, scale, ou
     the required size is allocated by torch for this call."""
     dev = _on_gpu(q, k_pool, v_pool, block_table, context_lens, out)
     _require(q.dim() == 3, "q must be [rows, n_heads, head_dim]")
-    _require(k_pool.dim() == 4 and v_pool.shape == k_pool.shape,
-             "pools must be [num_blocks, n_kv_heads, block_size, head_dim]")
+    _check_pools(k_pool, v_pool)
     _require(k_pool.dtype == q.dtype and v_pool.dtype == q.dtype, "q and pools must share one dtype")
     _require(block_table.dtype == torch.int32 and block_table.dim() == 2
              and block_table.shape[0] == q.shape[0], "block_table must be int32 [rows, max_blocks]")

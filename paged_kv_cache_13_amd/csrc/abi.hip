@@ -60,6 +60,8 @@ int plan_decode(const pkv_attn_desc *d, Plan *pl) {
   pl->group = d->n_heads / d->n_kv_heads;
   pl->partition = part;
   pl->max_parts = (cap + part - 1) / part;
+  // one workgroup per (partition, kv head, row) in a 1-D grid
+  if ((int64_t)pl->max_parts * d->n_kv_heads * d->rows > INT_MAX) return PKV_ERR_SHAPE;
   pl->log2_bs = log2i(d->block_size);
   pl->ws_bytes = 0;
   if (pl->max_parts > 1 && d->rows > 0)

@@ -154,6 +154,44 @@ __device__ __forceinline__ uint4 load16(const void *base, size_t byte_off) {
   return *reinterpret_cast<const uint4 *>(static_cast<const char *>(base) + byte_off);
 }
 
+// 16 bytes of one position's V row from a dimension-major tile: consecutive
+// elements are `stride` elements apart starting at element index `first`.
+template <typename T>
+__device__ __forceinline__ uint4 gather_v(const void *base, size_t first, int stride);
+template <>
+__device__ __forceinline__ uint4 gather_v<float>(const void *base, size_t first, int stride) {
+  const uint32_t *p = static_cast<const uint32_t *>(base) + first;
+  return make_uint4(p[0], p[stride], p[2 * stride], p[3 * stride]);
+}
+template <>
+__device__ __forceinline__ uint4 gather_v<uint16_t>(const void *base, size_t first, int stride) {
+  const uint16_t *p = static_cast<const uint16_t *>(base) + first;
+  uint32_t w[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    w[i] = (uint32_t)p[(2 * i) * stride] | ((uint32_t)p[(2 * i + 1) * stride] << 16);
+  return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+// Work item of this workgroup.  The grid is 1-D and ordered kv head fastest,
+// then row, then partition.  Workgroups are handed to the 8 XCDs round-robin
+// by linear id, so this order gives every XCD the same mix of full, partial
+// and empty partitions (with the partition index fastest, XCD k would get
+// only partition k of every row), and the mostly empty high partitions come
+// last in dispatch order.
+struct WorkItem {
+  int p, g, r;
+};
+__device__ __forceinline__ WorkItem work_item(const DecodeArgs &a) {
+  const unsigned id = blockIdx.x;
+  const unsigned rest = id / (unsigned)a.n_kv_heads;
+  WorkItem w;
+  w.g = (int)(id - rest * (unsigned)a.n_kv_heads);
+  w.p = (int)(rest / (unsigned)a.rows);
+  w.r = (int)(rest - (unsigned)w.p * (unsigned)a.rows);
+  return w;
+}
+
 template <typename T, int HD, int GP>
 __global__ __launch_bounds__(kThreads) void decode_partition(DecodeArgs a) {
   constexpr int ES = sizeof(T);
@@ -168,9 +206,8 @@ __global__ __launch_bounds__(kThreads) void decode_partition(DecodeArgs a) {
   __shared__ float s_acc[kWaves][GP][HD];
   extern __shared__ int32_t s_blk[];
 
-  const int p = blockIdx.x;
-  const int g = blockIdx.y;
-  const int r = blockIdx.z;
+  const WorkItem it = work_item(a);
+  const int p = it.p, g = it.g, r = it.r;
   const int tid = threadIdx.x;
   const int cap = a.max_blocks_per_row * a.block_size;
   int n = a.context_lens[r];
@@ -239,10 +276,12 @@ __global__ __launch_bounds__(kThreads) void decode_partition(DecodeArgs a) {
       vr[i] = make_uint4(0, 0, 0, 0);
       if (valid[i]) {
         const int32_t blk = s_blk[(t - start) >> a.log2_bs];
-        const size_t row = (((size_t)blk * tile_stride + g) << a.log2_bs) + (t & bmask);
-        const size_t off = (row * HD + c * EPL) * ES;
-        kr[i] = load16(a.k_pool, off);
-        vr[i] = load16(a.v_pool, off);
+        const size_t tile = (size_t)blk * tile_stride + g;
+        const size_t row = (tile << a.log2_bs) + (t & bmask);
+        kr[i] = load16(a.k_pool, (row * HD + c * EPL) * ES);
+        // V tile is dimension-major: element d of position o at [d][o]
+        vr[i] = gather_v<T>(a.v_pool, ((tile * HD + c * EPL) << a.log2_bs) + (t & bmask),
+                            a.block_size);
       }
     }
     // scores
@@ -364,9 +403,300 @@ __global__ __launch_bounds__(128) void decode_merge(DecodeArgs a) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// bf16 path on the matrix cores.
+//
+// A wave takes 32 consecutive positions of its partition per iteration.  The
+// GQA group (padded to 16 heads) is the N side of both contractions:
+//   scores  S[t][h]  = sum_d K[t][d] Q[h][d]      v_mfma_f32_16x16x32_bf16,
+//                      A = K rows (position-major tile), B = Q, two 16-row
+//                      tiles per 32 positions, head_dim / 32 k-steps each;
+//   output  O[d][h] += sum_t V[d][t] P[h][t]      same instruction, A = V
+//                      (dimension-major tile), B = P, head_dim / 16 d-tiles.
+// Row m of score tile tt is position 8*(m/4) + 4*tt + m%4 of the 32, so the
+// 4 accumulator rows a lane receives from the two tiles are 8 consecutive
+// positions 8*(lane/16) .. +7 for head lane%16 -- exactly the 8 k-values that
+// lane must supply as the B operand of the P.V product.  Scores, softmax
+// state and output rows of head h therefore all live in the lanes with
+// lane%16 == h, and nothing crosses lanes except the max over positions.
+// P is fed to the bf16 product as a hi + lo pair of bf16 values (16
+// significant bits), so the weights carry fp32-grade precision into the
+// fp32 accumulators.
+// ---------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+// All-reduce over the four 16-lane rows (lane bits 4 and 5).  Written with
+// ds_bpermute exchanges: this compiler folds the two results of a
+// v_permlane{16,32}_swap whose operands are the same value into one, which
+// breaks a swap-based all-reduce.
+__device__ __forceinline__ float max_across_rows(float x) {
+  x = fmaxf(x, __shfl_xor(x, 32));
+  return fmaxf(x, __shfl_xor(x, 16));
+}
+
+__device__ __forceinline__ float sum_across_rows(float x) {
+  x += __shfl_xor(x, 32);
+  return x + __shfl_xor(x, 16);
+}
+
+__device__ __forceinline__ uint32_t bf16_bits_rne(float x) {  // finite x only
+  const uint32_t b = __builtin_bit_cast(uint32_t, x);
+  return (b + 0x7FFFu + ((b >> 16) & 1u)) >> 16;
+}
+
+__device__ __forceinline__ bf16x8_t ld_bf16x8(const void *base, size_t byte_off) {
+  return __builtin_bit_cast(bf16x8_t, load16(base, byte_off));
+}
+
+__device__ __forceinline__ bf16x8_t zero_bf16x8() { return __builtin_bit_cast(bf16x8_t, make_uint4(0, 0, 0, 0)); }
+
+// Keep the first `nv` (0..8) of 8 packed bf16 values, zero the rest (NaN-safe).
+__device__ __forceinline__ bf16x8_t keep_first(bf16x8_t v, int nv) {
+  uint4 w = __builtin_bit_cast(uint4, v);
+  uint32_t x[4] = {w.x, w.y, w.z, w.w};
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t lo = (2 * i < nv) ? 0x0000FFFFu : 0u;
+    const uint32_t hi = (2 * i + 1 < nv) ? 0xFFFF0000u : 0u;
+    x[i] &= (lo | hi);
+  }
+  return __builtin_bit_cast(bf16x8_t, make_uint4(x[0], x[1], x[2], x[3]));
+}
+
+template <int HD>
+struct MfmaTiles {
+  bf16x8_t k[2][HD / 32];  // score tiles x k-steps
+  bf16x8_t v[HD / 16];     // output d-tiles
+};
+
+// Issue the loads of one 32-position group.  Branch-free: positions at or
+// past `end` load from the partition's first position instead (always
+// mapped), and are masked where they are used, so the loads of the next group
+// can be in flight while this one is computed.
+template <int HD, int BS>
+__device__ __forceinline__ void mfma_load(MfmaTiles<HD> &T, const DecodeArgs &a, const int32_t *s_blk,
+                                          int g, int start, int end, int gbase, int lr, int lg) {
+  constexpr int KS = HD / 32, DT = HD / 16;
+  constexpr int LOG2_BS = BS == 8 ? 3 : (BS == 16 ? 4 : 5);
+  constexpr int bmask = BS - 1;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    int t = gbase + 8 * (lr >> 2) + 4 * tt + (lr & 3);
+    t = t < end ? t : start;
+    const int32_t blk = s_blk[(t - start) >> LOG2_BS];
+    const size_t row = (((size_t)blk * a.n_kv_heads + g) << LOG2_BS) + (t & bmask);
+    const char *kp = static_cast<const char *>(a.k_pool) + (row * HD + lg * 8) * 2;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) T.k[tt][i] = ld_bf16x8(kp, i * 64);
+  }
+  int t0 = gbase + 8 * lg;
+  t0 = t0 < end ? t0 : start;
+  const int32_t blk = s_blk[(t0 - start) >> LOG2_BS];
+  const size_t base = ((((size_t)blk * a.n_kv_heads + g) * HD + lr) << LOG2_BS) + (t0 & bmask);
+  const char *vp = static_cast<const char *>(a.v_pool) + base * 2;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) T.v[dt] = ld_bf16x8(vp, dt * 16 * BS * 2);
+}
+
+// Online-softmax step over one loaded group (see the block comment above).
+template <int HD>
+__device__ __forceinline__ void mfma_compute(MfmaTiles<HD> &T, const bf16x8_t *qb, f32x4_t *acc, float &m,
+                                             float &l, float c, int end, int gbase, int lg) {
+  constexpr int KS = HD / 32, DT = HD / 16;
+  f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int i = 0; i < KS; ++i)
+      sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(T.k[tt][i], qb[i], sacc[tt], 0, 0, 0);
+
+  // this lane: head lane%16, positions gbase + 8*lg + e with e = 4*tt + j
+  const int tl = gbase + 8 * lg;
+  float s[8];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s[4 * tt + j] = (tl + 4 * tt + j < end) ? sacc[tt][j] * c : -INFINITY;
+  float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+  mx = max_across_rows(mx);
+  const float m_new = fmaxf(m, mx);
+  const float alpha = (m == m_new) ? 1.f : exp2_fast(m - m_new);
+  m = m_new;
+  float pv[8], psum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    pv[e] = exp2_fast(s[e] - m_new);
+    psum += pv[e];
+  }
+  l = l * alpha + psum;
+  if (__any(alpha != 1.f)) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+  }
+  uint32_t hw[4], lw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t h0 = bf16_bits_rne(pv[2 * i]), h1 = bf16_bits_rne(pv[2 * i + 1]);
+    const float r0 = pv[2 * i] - __builtin_bit_cast(float, h0 << 16);
+    const float r1 = pv[2 * i + 1] - __builtin_bit_cast(float, h1 << 16);
+    hw[i] = h0 | (h1 << 16);
+    lw[i] = bf16_bits_rne(r0) | (bf16_bits_rne(r1) << 16);
+  }
+  const bf16x8_t phi = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+  const bf16x8_t plo = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+  // The last group of a partition may hold positions past `end` (stale or
+  // NaN pool slots): their weights are 0, but 0 * NaN is NaN, so the V values
+  // themselves are zeroed.  Wave-uniform branch, taken once per partition.
+  if (gbase + 32 > end) {
+    int nv = end - tl;
+    nv = nv < 0 ? 0 : (nv > 8 ? 8 : nv);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) T.v[dt] = keep_first(T.v[dt], nv);
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(T.v[dt], phi, acc[dt], 0, 0, 0);
+    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(T.v[dt], plo, acc[dt], 0, 0, 0);
+  }
+}
+
+template <int HD, int BS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_partition_mfma(DecodeArgs a) {
+  constexpr int KS = HD / 32, DT = HD / 16, GT = 32;
+  __shared__ float s_m[kWaves][16];
+  __shared__ float s_l[kWaves][16];
+  __shared__ float s_acc[kWaves][16][HD];
+  extern __shared__ int32_t s_blk[];
+
+  const WorkItem it = work_item(a);
+  const int p = it.p, g = it.g, r = it.r;
+  const int tid = threadIdx.x;
+  const int cap = a.max_blocks_per_row * a.block_size;
+  int n = a.context_lens[r];
+  n = n < 0 ? 0 : (n > cap ? cap : n);
+  const int P = a.partition_tokens;
+  const int start = p * P;
+  const int group = a.group;
+  if (start >= n) {
+    if (p == 0) {
+      for (int idx = tid; idx < group * HD; idx += kThreads) {
+        const int j = idx / HD, d = idx % HD;
+        store_out(a.out, a.out_dtype, ((size_t)r * a.n_heads + g * group + j) * HD + d, 0.f);
+      }
+    }
+    return;
+  }
+  const int end = min(n, start + P);
+  const bool single = n <= P;
+  const int nblk = (end - start + a.block_size - 1) >> a.log2_bs;
+  const int32_t *table_row = a.block_table + (size_t)r * a.max_blocks_per_row + (start >> a.log2_bs);
+  for (int i = tid; i < nblk; i += kThreads) {
+    int64_t b = table_row[i];
+    b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
+    s_blk[i] = (int32_t)b;
+  }
+
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+  const int lr = lane & 15;  // head of the group (N index)
+  const int lg = lane >> 4;  // k-slot group
+
+  bf16x8_t qb[KS];
+#pragma unroll
+  for (int i = 0; i < KS; ++i)
+    qb[i] = lr < group
+                ? ld_bf16x8(a.q, (((size_t)r * a.n_heads + g * group + lr) * HD + (4 * i + lg) * 8) * 2)
+                : zero_bf16x8();
+  __syncthreads();
+
+  const float c = a.scale * kLog2e;
+  float m = -INFINITY, l = 0.f;
+  f32x4_t acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  // Two tile sets, alternating: while one group is computed the next one's
+  // loads are in flight.  Uniform control flow only.
+  constexpr int kStep = kWaves * GT;
+  MfmaTiles<HD> A, B;
+  int gb = start + wave * GT;
+  if (gb < end) {
+    mfma_load<HD, BS>(A, a, s_blk, g, start, end, gb, lr, lg);
+    while (true) {
+      if (gb + kStep >= end) {
+        mfma_compute<HD>(A, qb, acc, m, l, c, end, gb, lg);
+        break;
+      }
+      mfma_load<HD, BS>(B, a, s_blk, g, start, end, gb + kStep, lr, lg);
+      mfma_compute<HD>(A, qb, acc, m, l, c, end, gb, lg);
+      gb += kStep;
+      if (gb + kStep >= end) {
+        mfma_compute<HD>(B, qb, acc, m, l, c, end, gb, lg);
+        break;
+      }
+      mfma_load<HD, BS>(A, a, s_blk, g, start, end, gb + kStep, lr, lg);
+      mfma_compute<HD>(B, qb, acc, m, l, c, end, gb, lg);
+      gb += kStep;
+    }
+  }
+
+  // per-wave state -> LDS; lanes of head lr hold output dims 16*dt + 4*lg + j
+  l = sum_across_rows(l);
+  if (lr < group) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) s_acc[wave][lr][16 * dt + 4 * lg + j] = acc[dt][j];
+    if (lg == 0) {
+      s_m[wave][lr] = m;
+      s_l[wave][lr] = l;
+    }
+  }
+  __syncthreads();
+
+  const WsLayout ws = single ? WsLayout{} : ws_layout(a.rows, a.n_heads, a.max_parts, HD);
+  for (int idx = tid; idx < group * HD; idx += kThreads) {
+    const int j = idx / HD, d = idx % HD;
+    float M = -INFINITY;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) M = fmaxf(M, s_m[w][j]);
+    float L = 0.f, O = 0.f;
+#pragma unroll
+    for (int w = 0; w < kWaves; ++w) {
+      const float mw = s_m[w][j];
+      const float wt = (mw == -INFINITY) ? 0.f : exp2_fast(mw - M);
+      L = fmaf(s_l[w][j], wt, L);
+      O = fmaf(s_acc[w][j][d], wt, O);
+    }
+    const int h = g * group + j;
+    if (single) {
+      store_out(a.out, a.out_dtype, ((size_t)r * a.n_heads + h) * HD + d, O / L);
+    } else {
+      const size_t slot = ((size_t)r * a.n_heads + h) * a.max_parts + p;
+      a.ws[ws.acc_off + slot * HD + d] = O;
+      if (d == 0) {
+        a.ws[ws.m_off + slot] = M;
+        a.ws[ws.l_off + slot] = L;
+      }
+    }
+  }
+}
+
+template <int HD, int BS>
+hipError_t launch_mfma(const DecodeArgs &a, hipStream_t stream) {
+  const dim3 grid((unsigned)a.max_parts * a.n_kv_heads * a.rows);
+  const size_t lds = (size_t)(a.partition_tokens >> a.log2_bs) * sizeof(int32_t);
+  hipLaunchKernelGGL((decode_partition_mfma<HD, BS>), grid, dim3(kThreads), lds, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.max_parts <= 1) return e;
+  hipLaunchKernelGGL(decode_merge, dim3((unsigned)a.rows * a.n_heads), dim3(128), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <typename T, int HD, int GP>
 hipError_t launch_t(const DecodeArgs &a, hipStream_t stream) {
-  dim3 grid(a.max_parts, a.n_kv_heads, a.rows);
+  const dim3 grid((unsigned)a.max_parts * a.n_kv_heads * a.rows);
   const size_t lds = (size_t)(a.partition_tokens >> a.log2_bs) * sizeof(int32_t);
   hipLaunchKernelGGL((decode_partition<T, HD, GP>), grid, dim3(kThreads), lds, stream, a);
   hipError_t e = hipGetLastError();
@@ -398,6 +728,16 @@ hipError_t launch_dt(const DecodeArgs &a, hipStream_t s) {
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   if (a.dtype == kF32) return launch_dt<float>(a, stream);
+  if (a.head_dim == 128 || a.head_dim == 64) {
+    if (a.head_dim == 128) {
+      if (a.block_size == 8) return launch_mfma<128, 8>(a, stream);
+      if (a.block_size == 16) return launch_mfma<128, 16>(a, stream);
+      return launch_mfma<128, 32>(a, stream);
+    }
+    if (a.block_size == 8) return launch_mfma<64, 8>(a, stream);
+    if (a.block_size == 16) return launch_mfma<64, 16>(a, stream);
+    return launch_mfma<64, 32>(a, stream);
+  }
   return launch_dt<uint16_t>(a, stream);
 }
 

@@ -145,7 +145,7 @@ class DecodeBatch:
     cfg: DecodeConfig
     q: torch.Tensor             # [rows, n_heads, head_dim]
     k_pool: torch.Tensor        # [num_blocks, n_kv_heads, block_size, head_dim]
-    v_pool: torch.Tensor
+    v_pool: torch.Tensor        # [num_blocks, n_kv_heads, head_dim, block_size]
     block_table: torch.Tensor   # [rows, max_blocks_per_row] int32
     context_lens: torch.Tensor  # [rows] int32
     ctx_host: np.ndarray        # host copy of the lengths (drawn here, never read back)
@@ -202,10 +202,9 @@ def make_batch(cfg: DecodeConfig, device="cpu", seed: Optional[int] = None,
     dt = torch_dtype(cfg.dtype)
     gen = torch.Generator(device=device)
     gen.manual_seed(seed)
-    shape_pool = (nb, cfg.n_kv_heads, bs, cfg.head_dim)
     q = _fill_normal((cfg.rows, cfg.n_heads, cfg.head_dim), dt, device, gen, cfg.value_scale)
-    k_pool = _fill_normal(shape_pool, dt, device, gen, cfg.value_scale)
-    v_pool = _fill_normal(shape_pool, dt, device, gen, cfg.value_scale)
+    k_pool = _fill_normal((nb, cfg.n_kv_heads, bs, cfg.head_dim), dt, device, gen, cfg.value_scale)
+    v_pool = _fill_normal((nb, cfg.n_kv_heads, cfg.head_dim, bs), dt, device, gen, cfg.value_scale)
     if poison:
         unused = np.ones((nb, bs), dtype=bool)
         unused[owned] = False
@@ -213,9 +212,9 @@ def make_batch(cfg: DecodeConfig, device="cpu", seed: Optional[int] = None,
             n = int(lens[r])
             if n % bs and need[r]:
                 unused[table[r, need[r] - 1], n % bs:] = True
-        mask = torch.from_numpy(unused).to(device)[:, None, :, None]
-        k_pool.masked_fill_(mask, float("nan"))
-        v_pool.masked_fill_(mask, float("nan"))
+        mask = torch.from_numpy(unused).to(device)
+        k_pool.masked_fill_(mask[:, None, :, None], float("nan"))
+        v_pool.masked_fill_(mask[:, None, None, :], float("nan"))
     return DecodeBatch(cfg=cfg, q=q, k_pool=k_pool, v_pool=v_pool,
                        block_table=torch.from_numpy(table).to(device),
                        context_lens=torch.from_numpy(lens).to(device),
@@ -250,9 +249,10 @@ class DecodeRun:
         self.gen.manual_seed(seed)
         self.alloc = BlockAllocator(self.num_blocks, self.rng)
         self.poison_block = self.alloc.allocate()
-        shape = (self.num_blocks, n_kv_heads, block_size, head_dim)
-        self.k_pool = torch.full(shape, float("nan"), dtype=self.dtype, device=device)
-        self.v_pool = torch.full(shape, float("nan"), dtype=self.dtype, device=device)
+        self.k_pool = torch.full((self.num_blocks, n_kv_heads, block_size, head_dim), float("nan"),
+                                 dtype=self.dtype, device=device)
+        self.v_pool = torch.full((self.num_blocks, n_kv_heads, head_dim, block_size), float("nan"),
+                                 dtype=self.dtype, device=device)
         self.table_host = np.full((rows, self.max_blocks_per_row), self.poison_block,
                                   dtype=np.int32)
         self.ctx_host = np.zeros(rows, dtype=np.int32)

@@ -55,7 +55,7 @@ def test_scatter_is_bit_exact(dtype, hd, bs, nkv):
     slots = rng.choice(nb * bs, size=T, replace=False).astype(np.int64)
     slots[rng.choice(T, size=17, replace=False)] = -1
     kp = bits((nb, nkv, bs, hd)).view(tdt)
-    vp = bits((nb, nkv, bs, hd)).view(tdt)
+    vp = bits((nb, nkv, hd, bs)).view(tdt)
     kp_d, vp_d = kp.to(DEV), vp.to(DEV)
     pkv.reshape_and_cache(k.to(DEV), v.to(DEV), torch.from_numpy(slots).to(DEV), kp_d, vp_d)
     torch.cuda.synchronize()
@@ -151,7 +151,7 @@ def test_read_edge_lengths(bs):
     assert_close(got, ref, what="edge lengths", **TOL[torch.float32])
     assert np.array_equal(got[0], np.zeros_like(got[0]))  # empty row reads zeros
     # one position: softmax weight exactly 1, output is that V row exactly
-    v0 = b.v_pool[int(b.table_host[1, 0]), :, 0, :].cpu().numpy()
+    v0 = b.v_pool[int(b.table_host[1, 0]), :, :, 0].cpu().numpy()
     assert np.array_equal(got[1], np.repeat(v0, 4, axis=0))
 
 
@@ -231,3 +231,31 @@ def test_decode_run_sweep(rows, bs):
     # run saving: sum of widths over sum of held tiles
     widths = np.arange(513, 513 + steps)
     assert stats.saving == pytest.approx(widths.sum() / np.minimum(bs, widths).sum())
+
+
+# ---------------------------------------------------------------------------
+# closed forms on the GPU path
+# ---------------------------------------------------------------------------
+
+@pytest.mark.parametrize("dtype,hd", [("bf16", 128), ("bf16", 64), ("bf16", 16), ("f32", 128)])
+def test_read_constant_values_give_that_constant(dtype, hd):
+    # V == c everywhere: every softmax weighting returns c; the weights in the
+    # numerator and the sum in the denominator must agree
+    cfg = small_cfg(dtype, rows=8, H=32, KV=8, hd=hd, bs=16, lo=1, hi=3000, seed=21)
+    b = synth.make_batch(cfg, device=DEV)
+    c = torch.linspace(-2, 2, hd, device=DEV).to(b.v_pool.dtype)  # exact in bf16
+    b.v_pool.copy_(c[None, None, :, None].expand_as(b.v_pool))
+    got = gpu_read(b, out_dtype=torch.float32).cpu()
+    expect = c.float().cpu()[None, None, :].expand_as(got)
+    assert_close(got, expect, what="constant V", atol=1e-6, rtol=1e-5)
+
+
+@pytest.mark.parametrize("dtype,hd", [("bf16", 128), ("f32", 64)])
+def test_read_zero_query_gives_mean_of_values(dtype, hd):
+    cfg = small_cfg(dtype, rows=6, H=16, KV=4, hd=hd, bs=16, lo=1, hi=2500, seed=22)
+    b = synth.make_batch(cfg, device=DEV)
+    b.q.zero_()
+    got = gpu_read(b, out_dtype=torch.float32).cpu().numpy()
+    ref = oracle_read(b)
+    # uniform weights: the oracle's output is the plain mean of V over the row
+    assert_close(got, ref, what="zero query", **TOL[torch.float32])
