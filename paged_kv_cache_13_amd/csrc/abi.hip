@@ -35,6 +35,7 @@ bool pool_fits(int64_t num_blocks, int32_t bs, int32_t n_kv, int32_t hd, int32_t
 
 struct Plan {
   int32_t group, partition, max_parts, log2_bs;
+  int32_t stream, cg_min;
   size_t ws_bytes;
 };
 
@@ -59,11 +60,27 @@ int plan_decode(const pkv_attn_desc *d, Plan *pl) {
   if (part / d->block_size > kMaxPartitionBlocks) return PKV_ERR_PARTITION;
   pl->group = d->n_heads / d->n_kv_heads;
   pl->partition = part;
+  pl->log2_bs = log2i(d->block_size);
+  pl->ws_bytes = 0;
+  // bf16 with head_dim 64/128 runs the balanced stream decomposition when the
+  // plan kernel can hold the rows and the group count fits in 31 bits;
+  // everything else runs one workgroup per (partition, kv head, row).
+  const int64_t cap_groups = (cap + pkv::kGroupPositions - 1) / pkv::kGroupPositions;
+  pl->stream = d->dtype == PKV_BF16 && (d->head_dim == 64 || d->head_dim == 128) &&
+               d->rows <= pkv::kPlanMaxRows &&
+               cap_groups * d->n_kv_heads * d->rows < (int64_t)INT_MAX;
+  if (pl->stream) {
+    pl->cg_min = (part + pkv::kGroupPositions - 1) / pkv::kGroupPositions;
+    pl->max_parts = (int32_t)((cap_groups + pl->cg_min - 1) / pl->cg_min + 1);
+    if (d->rows > 0)
+      pl->ws_bytes = pkv::stream_layout(d->rows, d->n_kv_heads, pl->group, d->head_dim, pl->max_parts).total *
+                     sizeof(int32_t);
+    return PKV_OK;
+  }
+  pl->cg_min = 0;
   pl->max_parts = (cap + part - 1) / part;
   // one workgroup per (partition, kv head, row) in a 1-D grid
   if ((int64_t)pl->max_parts * d->n_kv_heads * d->rows > INT_MAX) return PKV_ERR_SHAPE;
-  pl->log2_bs = log2i(d->block_size);
-  pl->ws_bytes = 0;
   if (pl->max_parts > 1 && d->rows > 0)
     pl->ws_bytes =
         pkv::ws_layout(d->rows, d->n_heads, pl->max_parts, d->head_dim).total_floats * sizeof(float);
@@ -154,6 +171,9 @@ int pkv_paged_attention(const pkv_attn_desc *d, const void *q, const void *k_poo
   a.max_blocks_per_row = d->max_blocks_per_row;
   a.partition_tokens = pl.partition;
   a.max_parts = pl.max_parts;
+  a.stream = pl.stream;
+  a.cg_min = pl.cg_min;
+  a.inplan = pl.stream && d->rows <= pkv::kWindowRows;
   a.num_blocks = d->num_blocks;
   a.dtype = d->dtype;
   a.out_dtype = d->out_dtype;

@@ -694,6 +694,625 @@ hipError_t launch_mfma(const DecodeArgs &a, hipStream_t stream) {
   return hipGetLastError();
 }
 
+// ---------------------------------------------------------------------------
+// Balanced stream decomposition of the bf16 read.
+//
+// The unit of work is a group of 32 consecutive positions of one (kv head,
+// row).  All groups, ordered by kv head, then row, then position, form one
+// stream; a tiny plan kernel prefix-sums the groups per row on the device
+// (no host sync) and cuts the stream into kStreamWaves equal contiguous
+// slices.  Each persistent wave walks its slice with the next group's K/V
+// and the group after next's block ids in flight, across row boundaries, so
+// no wave waits on a partition start-up and every wave does the same work
+// whatever the length mix.  A (kv head, row) covered by one wave is written
+// to `out` directly; one cut into several slices gets one partial (max, sum,
+// rescaled acc) per slice, and the wave that writes the last partial (a
+// per-row counter, zeroed by the plan kernel on every call) merges them.
+// ---------------------------------------------------------------------------
+// Slice w of a stream of `total` groups cut into `waves` slices.
+__device__ __forceinline__ long long slice_start(long long w, long long total, long long waves) {
+  return w * total / waves;
+}
+// The slice holding group `pos`: the largest w with slice_start(w) <= pos.
+__device__ __forceinline__ long long slice_of(long long pos, long long total, long long waves) {
+  return ((pos + 1) * waves - 1) / total;
+}
+
+__global__ __launch_bounds__(1024) void decode_plan(DecodeArgs a) {
+  __shared__ int32_t s_gpre[kPlanMaxRows + 1];
+  __shared__ int32_t s_sum[1024];
+  const int tid = threadIdx.x;
+  const int rows = a.rows;
+  const int cap = a.max_blocks_per_row * a.block_size;
+  const StreamLayout L = stream_layout(rows, a.n_kv_heads, a.group, a.head_dim, a.max_parts);
+  int32_t *wsi = reinterpret_cast<int32_t *>(a.ws);
+  const int per = (rows + 1023) / 1024;
+  const int r0 = min(rows, tid * per), r1 = min(rows, r0 + per);
+  int local = 0;
+  for (int r = r0; r < r1; ++r) {
+    int n = a.context_lens[r];
+    n = n < 0 ? 0 : (n > cap ? cap : n);
+    s_gpre[r] = local;
+    local += (n + kGroupPositions - 1) / kGroupPositions;
+    if (n == 0) {  // an empty row reads zeros; no wave visits it
+      for (int idx = 0; idx < a.n_heads * a.head_dim; ++idx)
+        store_out(a.out, a.out_dtype, (size_t)r * a.n_heads * a.head_dim + idx, 0.f);
+    }
+  }
+  s_sum[tid] = local;
+  __syncthreads();
+  for (int off = 1; off < 1024; off <<= 1) {  // inclusive scan of the per-thread sums
+    const int v = tid >= off ? s_sum[tid - off] : 0;
+    __syncthreads();
+    s_sum[tid] += v;
+    __syncthreads();
+  }
+  const int base = tid ? s_sum[tid - 1] : 0;
+  for (int r = r0; r < r1; ++r) s_gpre[r] += base;
+  const int ngk = s_sum[1023];
+  if (tid == 0) s_gpre[rows] = ngk;
+  __syncthreads();
+  // Waves used: every one gets at least cg_min groups.  Wave w's slice is
+  // [floor(w * ng_all / waves), floor((w + 1) * ng_all / waves)), so slices
+  // differ by at most one group.
+  const long long ng_all = (long long)a.n_kv_heads * ngk;
+  long long waves = ng_all / max(a.cg_min, 1);
+  waves = waves < 1 ? 1 : (waves > kStreamWaves ? kStreamWaves : waves);
+  if (ng_all == 0) waves = 0;
+  if (tid == 0) {
+    wsi[L.hdr] = ngk;
+    wsi[L.hdr + 1] = (int)waves;
+    wsi[L.hdr + 2] = 0;
+    wsi[L.hdr + 3] = 0;
+  }
+  for (int r = tid; r <= rows; r += 1024) wsi[L.gpre + r] = s_gpre[r];
+  const int pairs = a.n_kv_heads * rows;
+  for (int qi = tid; qi < pairs; qi += 1024) {
+    const int kvh = qi / rows, r = qi - kvh * rows;
+    const int ng = s_gpre[r + 1] - s_gpre[r];
+    if (ng == 0) continue;
+    const long long S = (long long)kvh * ngk + s_gpre[r], E = S + ng;
+    for (long long w = slice_of(S, ng_all, waves); w < waves; ++w) {  // waves whose slice starts here
+      const long long st = slice_start(w, ng_all, waves);
+      if (st >= E) break;
+      if (st < S) continue;
+      wsi[L.first_pos + 2 * w] = qi;
+      wsi[L.first_pos + 2 * w + 1] = (int)(st - S);
+    }
+  }
+}
+
+// Position of one group of a (kv head, row) stream, plus what its segment
+// end needs.  Wave-uniform.
+struct Cursor {
+  int kvh, r, j, n, ng, part, nparts, idx;
+};
+
+// Lengths and group prefixes of kWindowRows consecutive rows, staged in LDS
+// so that moving a cursor to another row costs LDS reads only (lgkmcnt),
+// never a global load the in-flight K/V loads would have to drain behind.
+struct RowWindow {
+  int r0;
+  int32_t *ctx, *gpre;  // LDS, kWindowRows each
+};
+
+__device__ __forceinline__ void window_cover(RowWindow &win, const DecodeArgs &a, const int32_t *wsi,
+                                             const StreamLayout &L, int r, int lane, int cap) {
+  if (r < win.r0 || r >= win.r0 + kWindowRows) {  // rare: a wave crossing many rows
+    win.r0 = r;
+    for (int i = lane; i < kWindowRows; i += kWave) {
+      const int rr = r + i;
+      int n = rr < a.rows ? a.context_lens[rr] : 0;
+      win.ctx[i] = n < 0 ? 0 : (n > cap ? cap : n);
+      win.gpre[i] = rr <= a.rows ? wsi[L.gpre + rr] : 0;
+    }
+    __syncthreads();  // one wave per workgroup: orders the LDS writes before the reads
+  }
+}
+
+// Fill the row fields of a cursor whose kv head, row and group are set.
+// Slice numbers follow slice_of, so part/nparts name this piece of the row.
+__device__ __forceinline__ void cursor_row(Cursor &c, RowWindow &win, int w, int ngk, long long ng_all,
+                                           long long waves) {
+  c.n = win.ctx[c.r - win.r0];
+  c.ng = (c.n + kGroupPositions - 1) / kGroupPositions;
+  const long long S = (long long)c.kvh * ngk + win.gpre[c.r - win.r0];
+  const int first = (int)slice_of(S, ng_all, waves), last = (int)slice_of(S + c.ng - 1, ng_all, waves);
+  c.part = w - first;
+  c.nparts = last - first + 1;
+}
+
+// Next group of this wave's slice (only called while one remains).
+__device__ __forceinline__ void cursor_next(Cursor &c, RowWindow &win, const DecodeArgs &a, const int32_t *wsi,
+                                            const StreamLayout &L, int w, int ngk, long long ng_all,
+                                            long long waves, int lane, int cap) {
+  ++c.idx;
+  if (c.j + 1 < c.ng) {
+    ++c.j;
+    return;
+  }
+  do {  // next row with positions (empty rows hold no group)
+    if (++c.r == a.rows) {
+      c.r = 0;
+      ++c.kvh;
+    }
+    window_cover(win, a, wsi, L, c.r, lane, cap);
+  } while (win.ctx[c.r - win.r0] == 0);
+  c.j = 0;
+  cursor_row(c, win, w, ngk, ng_all, waves);
+}
+
+// Inclusive prefix sum over the 64 lanes.
+__device__ __forceinline__ int wave_inclusive_scan(int x, int lane) {
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int y = __shfl_up(x, d);
+    if (lane >= d) x += y;
+  }
+  return x;
+}
+
+// In-kernel plan for batches of at most kWindowRows rows: every wave scans
+// the (clamped) lengths itself -- lane l owns rows 4l..4l+3 -- into its LDS
+// window, so no plan kernel runs and no plan is read back from memory.
+// Returns the groups per kv head.
+__device__ __forceinline__ int plan_in_wave(RowWindow &win, const DecodeArgs &a, int lane, int cap) {
+  int ng[4], n[4], sum = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int r = 4 * lane + i;
+    int x = r < a.rows ? a.context_lens[r] : 0;
+    x = x < 0 ? 0 : (x > cap ? cap : x);
+    n[i] = x;
+    ng[i] = (x + kGroupPositions - 1) / kGroupPositions;
+    sum += ng[i];
+  }
+  const int incl = wave_inclusive_scan(sum, lane);
+  int run = incl - sum;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    win.ctx[4 * lane + i] = n[i];
+    win.gpre[4 * lane + i] = run;
+    run += ng[i];
+  }
+  win.r0 = 0;
+  __syncthreads();  // one wave per workgroup: orders the LDS writes before the reads
+  return __shfl(incl, kWave - 1);
+}
+
+// Row (and group in it) holding group `rem` of a kv head's stream, from the
+// in-wave plan: lane l checks its rows 4l..4l+3.
+__device__ __forceinline__ void plan_locate(const RowWindow &win, int rem, int lane, int &r, int &j) {
+  int found = -1;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int rr = 4 * lane + i;
+    const int g0 = win.gpre[rr];
+    const int ng = (win.ctx[rr] + kGroupPositions - 1) / kGroupPositions;
+    if (ng > 0 && g0 <= rem && rem < g0 + ng) found = rr;
+  }
+  const unsigned long long hit = __ballot(found >= 0);
+  const int src = (int)__builtin_ctzll(hit);
+  r = __shfl(found, src);
+  j = rem - win.gpre[r];
+}
+
+struct GroupIds {
+  int32_t k0, k1, v;  // this lane's block ids: score tiles 0/1 rows, V chunk
+};
+
+template <int BS>
+__device__ __forceinline__ GroupIds load_ids(const DecodeArgs &a, const Cursor &c, int lr, int lg) {
+  constexpr int LOG2_BS = BS == 8 ? 3 : (BS == 16 ? 4 : 5);
+  const int t0 = c.j * kGroupPositions, last = c.n - 1;
+  const int tk0 = min(t0 + 8 * (lr >> 2) + (lr & 3), last);
+  const int tk1 = min(t0 + 8 * (lr >> 2) + 4 + (lr & 3), last);
+  const int tv = min(t0 + 8 * lg, last);
+  const int32_t *row = a.block_table + (size_t)c.r * a.max_blocks_per_row;
+  GroupIds ids;
+  ids.k0 = row[tk0 >> LOG2_BS];
+  ids.k1 = row[tk1 >> LOG2_BS];
+  ids.v = row[tv >> LOG2_BS];
+  return ids;
+}
+
+template <int HD, int BS>
+__device__ __forceinline__ void load_group_k(bf16x8_t (&k)[2][HD / 32], const DecodeArgs &a, const Cursor &c,
+                                             const GroupIds &ids, int lr, int lg) {
+  constexpr int KS = HD / 32;
+  constexpr int LOG2_BS = BS == 8 ? 3 : (BS == 16 ? 4 : 5);
+  constexpr int bmask = BS - 1;
+  const int t0 = c.j * kGroupPositions, last = c.n - 1;
+  const int64_t nb1 = a.num_blocks - 1;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int t = min(t0 + 8 * (lr >> 2) + 4 * tt + (lr & 3), last);
+    int64_t blk = tt == 0 ? ids.k0 : ids.k1;
+    blk = blk < 0 ? 0 : (blk > nb1 ? nb1 : blk);
+    const size_t row = (((size_t)blk * a.n_kv_heads + c.kvh) << LOG2_BS) + (t & bmask);
+    const char *kp = static_cast<const char *>(a.k_pool) + (row * HD + lg * 8) * 2;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) k[tt][i] = ld_bf16x8(kp, i * 64);
+  }
+}
+
+template <int HD, int BS>
+__device__ __forceinline__ void load_group_v(bf16x8_t (&v)[HD / 16], const DecodeArgs &a, const Cursor &c,
+                                             const GroupIds &ids, int lr, int lg) {
+  constexpr int DT = HD / 16;
+  constexpr int LOG2_BS = BS == 8 ? 3 : (BS == 16 ? 4 : 5);
+  constexpr int bmask = BS - 1;
+  const int t0 = c.j * kGroupPositions, last = c.n - 1;
+  const int64_t nb1 = a.num_blocks - 1;
+  const int tv = min(t0 + 8 * lg, last) & ~7;
+  int64_t blk = ids.v;
+  blk = blk < 0 ? 0 : (blk > nb1 ? nb1 : blk);
+  const size_t base = ((((size_t)blk * a.n_kv_heads + c.kvh) * HD + lr) << LOG2_BS) + (tv & bmask);
+  const char *vp = static_cast<const char *>(a.v_pool) + base * 2;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) v[dt] = ld_bf16x8(vp, dt * 16 * BS * 2);
+}
+
+// Scores of one group: two 16x16 tiles (see the P.V layout note above).
+template <int HD>
+__device__ __forceinline__ void group_scores(const bf16x8_t (&k)[2][HD / 32], const bf16x8_t *qb,
+                                             f32x4_t (&sacc)[2]) {
+  constexpr int KS = HD / 32;
+  sacc[0] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  sacc[1] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int i = 0; i < KS; ++i) sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k[tt][i], qb[i], sacc[tt], 0, 0, 0);
+}
+
+// Online-softmax update and P.V of one group from its scores.
+template <int HD>
+__device__ __forceinline__ void group_softmax_pv(const f32x4_t (&sacc)[2], bf16x8_t (&v)[HD / 16], f32x4_t *acc,
+                                                 float &m, float &l, float c, int end, int gbase, int lg) {
+  constexpr int DT = HD / 16;
+  const int tl = gbase + 8 * lg;
+  float s[8];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s[4 * tt + j] = (tl + 4 * tt + j < end) ? sacc[tt][j] * c : -INFINITY;
+  float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+  mx = max_across_rows(mx);
+  const float m_new = fmaxf(m, mx);
+  const float alpha = (m == m_new) ? 1.f : exp2_fast(m - m_new);
+  m = m_new;
+  float pv[8], psum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    pv[e] = exp2_fast(s[e] - m_new);
+    psum += pv[e];
+  }
+  l = l * alpha + psum;
+  if (__any(alpha != 1.f)) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+  }
+  uint32_t hw[4], lw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t h0 = bf16_bits_rne(pv[2 * i]), h1 = bf16_bits_rne(pv[2 * i + 1]);
+    const float r0 = pv[2 * i] - __builtin_bit_cast(float, h0 << 16);
+    const float r1 = pv[2 * i + 1] - __builtin_bit_cast(float, h1 << 16);
+    hw[i] = h0 | (h1 << 16);
+    lw[i] = bf16_bits_rne(r0) | (bf16_bits_rne(r1) << 16);
+  }
+  const bf16x8_t phi = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+  const bf16x8_t plo = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+  if (gbase + 32 > end) {  // positions past the row end: zero their (possibly NaN) V
+    int nv = end - tl;
+    nv = nv < 0 ? 0 : (nv > 8 ? 8 : nv);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) v[dt] = keep_first(v[dt], nv);
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v[dt], phi, acc[dt], 0, 0, 0);
+    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v[dt], plo, acc[dt], 0, 0, 0);
+  }
+}
+
+template <int HD>
+__device__ __forceinline__ void write_out_rows(const DecodeArgs &a, const Cursor &c, const f32x4_t *o,
+                                               float inv, int lr, int lg) {
+  constexpr int DT = HD / 16;
+  const size_t base = ((size_t)c.r * a.n_heads + c.kvh * a.group + lr) * HD + 4 * lg;
+  if (a.out_dtype == kF32) {
+    float *out = static_cast<float *>(a.out) + base;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      *reinterpret_cast<f32x4_t *>(out + 16 * dt) = o[dt] * inv;
+  } else {
+    uint16_t *out = static_cast<uint16_t *>(a.out) + base;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint32_t w0 = f32_to_bf16_rne(o[dt][0] * inv) | ((uint32_t)f32_to_bf16_rne(o[dt][1] * inv) << 16);
+      const uint32_t w1 = f32_to_bf16_rne(o[dt][2] * inv) | ((uint32_t)f32_to_bf16_rne(o[dt][3] * inv) << 16);
+      *reinterpret_cast<uint2 *>(out + 16 * dt) = make_uint2(w0, w1);
+    }
+  }
+}
+
+// End of one (kv head, row) slice: write the output, or, for a row cut
+// into several slices, this slice's partial (max, sum, rescaled acc) for
+// decode_stream_merge.  Plain stores: the merge runs as the next kernel.
+template <int HD>
+__device__ __forceinline__ void segment_end(const DecodeArgs &a, const StreamLayout &L, const Cursor &c,
+                                            f32x4_t *acc, float &m, float &l, int lr, int lg) {
+  constexpr int DT = HD / 16;
+  const int G = a.group;
+  const float lt = sum_across_rows(l);
+  if (c.nparts == 1) {
+    if (lr < G) write_out_rows<HD>(a, c, acc, 1.f / lt, lr, lg);
+  } else if (lr < G) {
+    const size_t pair = (size_t)c.kvh * a.rows + c.r;
+    float *slot = a.ws + L.partials + (pair * a.max_parts + c.part) * L.slot_stride;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4_t *>(slot + lr * HD + 16 * dt + 4 * lg) = acc[dt];
+    if (lg == 0) {
+      slot[G * HD + lr] = m;
+      slot[G * HD + G + lr] = lt;
+    }
+  }
+  m = -INFINITY;
+  l = 0.f;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+}
+
+// Combine the partials of every (kv head, row) the stream cut into several
+// slices: M = max_k m_k;  L = sum_k l_k 2^(m_k - M);
+// out = sum_k acc_k 2^(m_k - M) / L.  One workgroup per (kv head, row);
+// rows in one slice were written by the stream kernel already.  The maxima
+// are read first (one independent load each), then the weighted sums.
+constexpr int kMergeMaxParts = 8;
+__global__ __launch_bounds__(256) void decode_stream_merge(DecodeArgs a) {
+  const StreamLayout L = stream_layout(a.rows, a.n_kv_heads, a.group, a.head_dim, a.max_parts);
+  const int32_t *wsi = reinterpret_cast<const int32_t *>(a.ws);
+  const int pair = blockIdx.x;
+  const int kvh = pair / a.rows, r = pair - kvh * a.rows;
+  int ngk, g0, ng;
+  long long waves;
+  if (a.inplan) {
+    // groups per kv head and before row r, by a block reduction over the
+    // (at most 256) clamped lengths
+    __shared__ int s_red[2][256 / kWave];
+    const int cap = a.max_blocks_per_row * a.block_size;
+    const int t = threadIdx.x;
+    int x = t < a.rows ? a.context_lens[t] : 0;
+    x = x < 0 ? 0 : (x > cap ? cap : x);
+    const int gx = (x + kGroupPositions - 1) / kGroupPositions;
+    int tot = gx, pre = t < r ? gx : 0;
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      tot += __shfl_xor(tot, d);
+      pre += __shfl_xor(pre, d);
+    }
+    if ((t & (kWave - 1)) == 0) {
+      s_red[0][t / kWave] = tot;
+      s_red[1][t / kWave] = pre;
+    }
+    __syncthreads();
+    ngk = s_red[0][0] + s_red[0][1] + s_red[0][2] + s_red[0][3];
+    g0 = s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
+    int xr = a.context_lens[r];
+    xr = xr < 0 ? 0 : (xr > cap ? cap : xr);
+    ng = (xr + kGroupPositions - 1) / kGroupPositions;
+    const long long all = (long long)a.n_kv_heads * ngk;
+    waves = all / max(a.cg_min, 1);
+    waves = waves < 1 ? 1 : (waves > kStreamWaves ? kStreamWaves : waves);
+  } else {
+    ngk = wsi[L.hdr];
+    waves = wsi[L.hdr + 1];
+    g0 = wsi[L.gpre + r];
+    ng = wsi[L.gpre + r + 1] - g0;
+  }
+  if (ng == 0) return;
+  const long long ng_all = (long long)a.n_kv_heads * ngk;
+  const long long S = (long long)kvh * ngk + g0;
+  const int nparts = (int)(slice_of(S + ng - 1, ng_all, waves) - slice_of(S, ng_all, waves) + 1);
+  if (nparts <= 1) return;
+  const int G = a.group, HD = a.head_dim;
+  const float *slots = a.ws + L.partials + (size_t)pair * a.max_parts * L.slot_stride;
+  for (int idx = threadIdx.x; idx < G * HD; idx += blockDim.x) {
+    const int j = idx / HD, d = idx - j * HD;
+    float M = -INFINITY, Lm = 0.f, O = 0.f;
+    for (int k0 = 0; k0 < nparts; k0 += kMergeMaxParts) {
+      const int kn = min(nparts - k0, kMergeMaxParts);
+      float mk[kMergeMaxParts], lk[kMergeMaxParts], ak[kMergeMaxParts];
+#pragma unroll
+      for (int k = 0; k < kMergeMaxParts; ++k) {
+        if (k < kn) {
+          const float *sk = slots + (size_t)(k0 + k) * L.slot_stride;
+          mk[k] = sk[G * HD + j];
+          lk[k] = sk[G * HD + G + j];
+          ak[k] = sk[j * HD + d];
+        }
+      }
+      float mn = M;
+#pragma unroll
+      for (int k = 0; k < kMergeMaxParts; ++k)
+        if (k < kn) mn = fmaxf(mn, mk[k]);
+      const float a0 = M == -INFINITY ? 0.f : exp2_fast(M - mn);
+      Lm *= a0;
+      O *= a0;
+#pragma unroll
+      for (int k = 0; k < kMergeMaxParts; ++k) {
+        if (k < kn) {
+          const float wk = exp2_fast(mk[k] - mn);
+          Lm = fmaf(lk[k], wk, Lm);
+          O = fmaf(ak[k], wk, O);
+        }
+      }
+      M = mn;
+    }
+    store_out(a.out, a.out_dtype, ((size_t)r * a.n_heads + kvh * G + j) * HD + d, O / Lm);
+  }
+}
+
+// Stage one group's K and V into this wave's LDS buffer with direct-to-LDS
+// loads (no VGPRs): each 16-byte-per-lane load lands as one contiguous 1 KiB
+// row of the buffer, lane l at offset 16*l -- the layout the matrix-core
+// operands are read back in.
+template <int HD, int BS>
+__device__ __forceinline__ void stage_group(uint4 *s_k, uint4 *s_v, const DecodeArgs &a, const Cursor &c,
+                                            const GroupIds &ids, int lane, int lr, int lg) {
+  constexpr int KS = HD / 32, DT = HD / 16;
+  constexpr int LOG2_BS = BS == 8 ? 3 : (BS == 16 ? 4 : 5);
+  constexpr int bmask = BS - 1;
+  const int t0 = c.j * kGroupPositions, last = c.n - 1;
+  const int64_t nb1 = a.num_blocks - 1;
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt) {
+    const int t = min(t0 + 8 * (lr >> 2) + 4 * tt + (lr & 3), last);
+    int64_t blk = tt == 0 ? ids.k0 : ids.k1;
+    blk = blk < 0 ? 0 : (blk > nb1 ? nb1 : blk);
+    const size_t row = (((size_t)blk * a.n_kv_heads + c.kvh) << LOG2_BS) + (t & bmask);
+    const char *kp = static_cast<const char *>(a.k_pool) + (row * HD + lg * 8) * 2;
+#pragma unroll
+    for (int i = 0; i < KS; ++i)
+      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(kp + i * 64),
+                                       (void __attribute__((address_space(3))) *)(s_k + (tt * KS + i) * kWave),
+                                       16, 0, 0);
+  }
+  const int tv = min(t0 + 8 * lg, last) & ~7;
+  int64_t blk = ids.v;
+  blk = blk < 0 ? 0 : (blk > nb1 ? nb1 : blk);
+  const size_t base = ((((size_t)blk * a.n_kv_heads + c.kvh) * HD + lr) << LOG2_BS) + (tv & bmask);
+  const char *vp = static_cast<const char *>(a.v_pool) + base * 2;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(vp + dt * 16 * BS * 2),
+                                     (void __attribute__((address_space(3))) *)(s_v + dt * kWave), 16, 0, 0);
+}
+
+template <int HD, int BS>
+__global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void decode_stream(DecodeArgs a) {
+  constexpr int KS = HD / 32, DT = HD / 16;
+  __shared__ uint4 s_k[2 * KS * kWave];
+  __shared__ uint4 s_v[DT * kWave];
+  __shared__ int32_t s_wctx[kWindowRows], s_wgpre[kWindowRows];
+  const StreamLayout L = stream_layout(a.rows, a.n_kv_heads, a.group, a.head_dim, a.max_parts);
+  const int32_t *wsi = reinterpret_cast<const int32_t *>(a.ws);
+  const int w = blockIdx.x;
+  const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
+  const int cap = a.max_blocks_per_row * a.block_size;
+  // Start-up round trip 1: header, this wave's start and the first row window
+  // (rows 0.. of the batch) are independent loads, issued together.
+  RowWindow win;
+  win.r0 = -(1 << 30);
+  win.ctx = s_wctx;
+  win.gpre = s_wgpre;
+  int ngk;
+  long long waves;
+  Cursor c0;
+  c0.idx = 0;
+  if (a.inplan) {
+    ngk = plan_in_wave(win, a, lane, cap);
+    const long long ng_all0 = (long long)a.n_kv_heads * ngk;
+    waves = ng_all0 / max(a.cg_min, 1);
+    waves = waves < 1 ? 1 : (waves > kStreamWaves ? kStreamWaves : waves);
+    if (w < a.rows && win.ctx[w] == 0) {  // an empty row reads zeros; no slice visits it
+      for (int idx = lane; idx < a.n_heads * a.head_dim; idx += kWave)
+        store_out(a.out, a.out_dtype, (size_t)w * a.n_heads * a.head_dim + idx, 0.f);
+    }
+    if (ng_all0 == 0 || w >= waves) return;
+    const long long st = slice_start(w, ng_all0, waves);
+    c0.kvh = (int)(st / ngk);
+    plan_locate(win, (int)(st - (long long)c0.kvh * ngk), lane, c0.r, c0.j);
+  } else {
+    window_cover(win, a, wsi, L, 0, lane, cap);
+    ngk = wsi[L.hdr];
+    waves = wsi[L.hdr + 1];
+    if (w >= waves) return;
+    const int qi = wsi[L.first_pos + 2 * w];
+    c0.kvh = qi / a.rows;
+    c0.r = qi - c0.kvh * a.rows;
+    c0.j = wsi[L.first_pos + 2 * w + 1];
+    window_cover(win, a, wsi, L, c0.r, lane, cap);
+  }
+  const long long ng_all = (long long)a.n_kv_heads * ngk;
+  const int total = (int)(slice_start(w + 1, ng_all, waves) - slice_start(w, ng_all, waves));
+  cursor_row(c0, win, w, ngk, ng_all, waves);
+
+  auto load_q = [&](const Cursor &c, bf16x8_t *qb) {
+#pragma unroll
+    for (int i = 0; i < KS; ++i)
+      qb[i] = lr < a.group ? ld_bf16x8(a.q, (((size_t)c.r * a.n_heads + c.kvh * a.group + lr) * HD + (4 * i + lg) * 8) * 2)
+                           : zero_bf16x8();
+  };
+  bf16x8_t qb[KS];
+  load_q(c0, qb);
+  const float cscale = a.scale * kLog2e;
+  float m = -INFINITY, l = 0.f;
+  f32x4_t acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  Cursor c1 = c0, c2;
+  if (total > 1) cursor_next(c1, win, a, wsi, L, w, ngk, ng_all, waves, lane, cap);
+  c2 = c1;
+  if (total > 2) cursor_next(c2, win, a, wsi, L, w, ngk, ng_all, waves, lane, cap);
+
+  GroupIds ids1;
+  {
+    const GroupIds ids0 = load_ids<BS>(a, c0, lr, lg);
+    stage_group<HD, BS>(s_k, s_v, a, c0, ids0, lane, lr, lg);
+  }
+  ids1 = load_ids<BS>(a, c1, lr, lg);
+
+  bf16x8_t kc[2][KS], vc[DT];
+  while (true) {
+    // the staged group is complete once every older load has returned; the
+    // block ids fetched after it may still be in flight
+    __builtin_amdgcn_s_waitcnt(0xF73);  // vmcnt(3)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < KS; ++i) kc[tt][i] = __builtin_bit_cast(bf16x8_t, s_k[(tt * KS + i) * kWave + lane]);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vc[dt] = __builtin_bit_cast(bf16x8_t, s_v[dt * kWave + lane]);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the buffer may be refilled
+    const bool last_group = c0.idx + 1 >= total;
+    GroupIds ids2;
+    if (!last_group) {
+      ids2 = load_ids<BS>(a, c2, lr, lg);
+      stage_group<HD, BS>(s_k, s_v, a, c1, ids1, lane, lr, lg);
+    }
+    f32x4_t sacc[2];
+    group_scores<HD>(kc, qb, sacc);
+    group_softmax_pv<HD>(sacc, vc, acc, m, l, cscale, c0.n, c0.j * kGroupPositions, lg);
+    if (c0.j == c0.ng - 1 || last_group) segment_end<HD>(a, L, c0, acc, m, l, lr, lg);
+    if (last_group) break;
+    const bool new_row = c1.r != c0.r || c1.kvh != c0.kvh;
+    c0 = c1;
+    c1 = c2;
+    if (c2.idx + 1 < total) cursor_next(c2, win, a, wsi, L, w, ngk, ng_all, waves, lane, cap);
+    ids1 = ids2;
+    if (new_row) load_q(c0, qb);
+  }
+}
+
+template <int HD, int BS>
+hipError_t launch_stream(const DecodeArgs &a, hipStream_t stream) {
+  hipError_t e;
+  if (!a.inplan) {
+    hipLaunchKernelGGL(decode_plan, dim3(1), dim3(1024), 0, stream, a);
+    e = hipGetLastError();
+    if (e != hipSuccess) return e;
+  }
+  hipLaunchKernelGGL((decode_stream<HD, BS>), dim3(kStreamWaves), dim3(kWave), 0, stream, a);
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(decode_stream_merge, dim3((unsigned)a.n_kv_heads * a.rows), dim3(256), 0, stream, a);
+  return hipGetLastError();
+}
+
 template <typename T, int HD, int GP>
 hipError_t launch_t(const DecodeArgs &a, hipStream_t stream) {
   const dim3 grid((unsigned)a.max_parts * a.n_kv_heads * a.rows);
@@ -728,6 +1347,16 @@ hipError_t launch_dt(const DecodeArgs &a, hipStream_t s) {
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
   if (a.dtype == kF32) return launch_dt<float>(a, stream);
+  if (a.stream) {
+    if (a.head_dim == 128) {
+      if (a.block_size == 8) return launch_stream<128, 8>(a, stream);
+      if (a.block_size == 16) return launch_stream<128, 16>(a, stream);
+      return launch_stream<128, 32>(a, stream);
+    }
+    if (a.block_size == 8) return launch_stream<64, 8>(a, stream);
+    if (a.block_size == 16) return launch_stream<64, 16>(a, stream);
+    return launch_stream<64, 32>(a, stream);
+  }
   if (a.head_dim == 128 || a.head_dim == 64) {
     if (a.head_dim == 128) {
       if (a.block_size == 8) return launch_mfma<128, 8>(a, stream);

@@ -16,9 +16,12 @@ struct DecodeArgs {
   const int32_t *block_table;
   const int32_t *context_lens;
   void *out;
-  float *ws;  // [3 regions] m, l, acc; null when max_parts == 1
+  float *ws;  // workspace: partition layout (ws_layout) or stream layout (stream_layout)
   int32_t rows, n_heads, n_kv_heads, group, head_dim, block_size, log2_bs;
   int32_t max_blocks_per_row, partition_tokens, max_parts;
+  int32_t stream;  // 1: balanced stream decomposition (bf16, head_dim 64/128)
+  int32_t cg_min;  // stream path: minimum 32-position groups per wave
+  int32_t inplan;  // stream path: rows <= kWindowRows, each wave plans for itself
   int64_t num_blocks;
   int32_t dtype, out_dtype;
   float scale;
@@ -38,6 +41,36 @@ __host__ __device__ inline WsLayout ws_layout(int32_t rows, int32_t n_heads, int
   w.acc_off = (2 * slots + 3) & ~(size_t)3;  // 16-byte aligned
   w.total_floats = w.acc_off + slots * head_dim;
   return w;
+}
+
+// Stream decomposition of the bf16 read: the groups of 32 positions of all
+// (kv head, row) pairs, in that order, are cut into kStreamWaves equal
+// contiguous slices, one per persistent wave.  Workspace, in 4-byte words:
+//   hdr[4]                 groups per kv head, groups per wave, waves used
+//   first_pos[2 * waves]   (kv head * rows + row, group) where each wave starts
+//   gpre[rows + 1]         exclusive prefix of groups per row
+//   counters[kv * rows]    partial slices written per (kv head, row)
+//   partials[kv * rows * max_parts][slot]  fp32 acc[group][hd], m[group], l[group]
+constexpr int kStreamWaves = 2048;
+constexpr int kWindowRows = 256;  // rows a wave keeps (and, if that is all, plans) in LDS
+constexpr int kPlanMaxRows = 8192;
+constexpr int kGroupPositions = 32;
+struct StreamLayout {
+  size_t hdr, first_pos, gpre, counters, partials, total;
+  size_t slot_stride;
+};
+__host__ __device__ inline size_t align4(size_t x) { return (x + 3) & ~(size_t)3; }
+__host__ __device__ inline StreamLayout stream_layout(int32_t rows, int32_t n_kv, int32_t group,
+                                                      int32_t head_dim, int32_t max_parts) {
+  StreamLayout L;
+  L.hdr = 0;
+  L.first_pos = 4;
+  L.gpre = L.first_pos + 2 * (size_t)kStreamWaves;
+  L.counters = L.gpre + (size_t)rows + 1;
+  L.partials = align4(L.counters + (size_t)n_kv * rows);
+  L.slot_stride = align4((size_t)group * (head_dim + 2));
+  L.total = L.partials + (size_t)n_kv * rows * max_parts * L.slot_stride;
+  return L;
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);

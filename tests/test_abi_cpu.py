@@ -58,21 +58,36 @@ def ws(lib, **kw):
     return lib.pkv_paged_attention_workspace_size(ctypes.byref(desc(**kw)))
 
 
-def test_workspace_size_values(lib):
-    # 64 rows x 32 heads x 8 partitions of 512: m and l (2 x 16384 floats), then
-    # 16384 rows of 128 fp32 partial sums
-    assert ws(lib) == (2 * 16384 + 16384 * 128) * 4
+def test_workspace_size_partition_layout(lib):
+    # fp32 reads split rows into partitions: 64 rows x 32 heads x 8 partitions
+    # of 512 -> m and l (2 x 16384 floats), then 16384 rows of 128 partial sums
+    assert ws(lib, dtype=0, out_dtype=0) == (2 * 16384 + 16384 * 128) * 4
     # one partition covers every row: no workspace
-    assert ws(lib, partition_tokens=4096) == 0
-    assert ws(lib, max_blocks_per_row=32) == 0
+    assert ws(lib, dtype=0, partition_tokens=4096) == 0
+    assert ws(lib, dtype=0, max_blocks_per_row=32) == 0
     # partitions of one block
-    assert ws(lib, partition_tokens=16, max_blocks_per_row=4, rows=1, n_heads=2, n_kv_heads=1,
-              head_dim=16) == (2 * 8 + 8 * 16) * 4
+    assert ws(lib, dtype=0, partition_tokens=16, max_blocks_per_row=4, rows=1, n_heads=2,
+              n_kv_heads=1, head_dim=16) == (2 * 8 + 8 * 16) * 4
     # odd slot count: the partial sums start 16-byte aligned
-    assert ws(lib, rows=1, n_heads=3, n_kv_heads=1, head_dim=16, partition_tokens=16,
+    assert ws(lib, dtype=0, rows=1, n_heads=3, n_kv_heads=1, head_dim=16, partition_tokens=16,
               max_blocks_per_row=3) == (20 + 9 * 16) * 4
+    # bf16 with head_dim 16 takes the same layout
+    assert ws(lib, head_dim=16) == (2 * 16384 + 16384 * 16) * 4
     assert lib.pkv_paged_attention_workspace_size(None) == 0
     assert ws(lib, head_dim=96) == 0  # invalid descriptors need nothing
+
+
+def test_workspace_size_stream_layout(lib):
+    # bf16, head_dim 128: header (4 words), 2048 wave starts (2 words each),
+    # 65 group prefixes, 8 x 64 row counters, aligned; then per (kv head, row)
+    # 128 / 16 + 1 = 9 partial slots of align4(4 heads x 130) = 520 floats
+    head = 4 + 2 * 2048 + 65 + 8 * 64
+    head += -head % 4
+    assert ws(lib) == (head + 8 * 64 * 9 * 520) * 4
+    # the stream layout always needs its header, even when no row can split
+    assert ws(lib, partition_tokens=4096) == (head + 8 * 64 * 2 * 520) * 4
+    # more rows than the plan kernel scans: back to partitions
+    assert ws(lib, rows=9000, max_blocks_per_row=32) == 0
 
 
 def attn(lib, d, q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, cl=FAKE, out=FAKE, wsp=FAKE, wsb=1 << 40):

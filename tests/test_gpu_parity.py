@@ -169,8 +169,12 @@ def test_read_block_permutation_is_bitwise_invariant():
     assert torch.equal(base, got)
 
 
-def test_read_rows_are_independent_bitwise():
-    cfg = small_cfg("bf16", rows=6, H=32, KV=8, hd=128, bs=16, lo=1, hi=2000, seed=3)
+@pytest.mark.parametrize("dtype,hd", [("bf16", 128), ("f32", 64)])
+def test_read_rows_are_independent(dtype, hd):
+    # permuting and padding the batch leaves every row's result in place (the
+    # bf16 path balances work over the whole batch, so where a row is split --
+    # and hence its last bits -- may move; the fp32 path splits per row)
+    cfg = small_cfg(dtype, rows=6, H=32, KV=8, hd=hd, bs=16, lo=1, hi=2000, seed=3)
     b = synth.make_batch(cfg, device=DEV)
     base = gpu_read(b, out_dtype=torch.float32)
     order = torch.tensor([5, 3, 1, 0, 2, 4, 0, 1], device=DEV)  # permuted and padded
@@ -180,7 +184,20 @@ def test_read_rows_are_independent_bitwise():
     b2.context_lens = b.context_lens[order].contiguous()
     b2.cfg = cfg.replace(rows=8)
     got = gpu_read(b2, out_dtype=torch.float32)
-    assert torch.equal(base[order], got)
+    if dtype == "f32":
+        assert torch.equal(base[order], got)
+    else:
+        assert_close(got.cpu(), base[order].cpu(), what="rows", atol=2e-6, rtol=1e-5)
+
+
+@pytest.mark.parametrize("name", ["llama3_8b_layer", "skewed_long"])
+def test_read_is_deterministic(name):
+    # same inputs, same bits: split points depend only on the inputs and the
+    # partials of a split row are merged in a fixed order
+    b = synth.make_batch(synth.CONFIGS[name], device=DEV)
+    first = gpu_read(b, out_dtype=torch.float32)
+    for _ in range(3):
+        assert torch.equal(first, gpu_read(b, out_dtype=torch.float32))
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -259,3 +276,39 @@ def test_read_zero_query_gives_mean_of_values(dtype, hd):
     ref = oracle_read(b)
     # uniform weights: the oracle's output is the plain mean of V over the row
     assert_close(got, ref, what="zero query", **TOL[torch.float32])
+
+
+@pytest.mark.parametrize("bs", [8, 16, 32])
+@pytest.mark.parametrize("hd", [64, 128])
+def test_read_edge_lengths_bf16(bs, hd):
+    # the bf16 path splits work over the whole batch: empty rows, one-position
+    # rows, block-boundary rows and one row filling its table, in one batch
+    lens = [0, 1, 31, 32, 33, bs - 1, bs, bs + 1, 0, 511, 512, 513, 2000, 16 * 64]
+    cap = max(lens)
+    cfg = synth.DecodeConfig("edge16", "bf16", rows=len(lens), n_heads=16, n_kv_heads=4, head_dim=hd,
+                             block_size=bs, ctx=("fixed", tuple(lens)), pool=("factor", 1.5),
+                             max_ctx=cap, seed=6)
+    b = synth.make_batch(cfg, device=DEV)
+    ref = oracle_read(b)
+    for part in (0, bs, 64 * bs):
+        got = gpu_read(b, out_dtype=torch.float32, partition=part).cpu().numpy()
+        assert_close(got, ref, what="bf16 edge lengths P=%d" % part, **TOL[torch.float32])
+        assert np.array_equal(got[0], np.zeros_like(got[0]))
+        assert np.array_equal(got[8], np.zeros_like(got[8]))
+
+
+@pytest.mark.parametrize("rows", [257, 600])
+def test_read_many_rows(rows):
+    # more rows than a wave plans for itself: the plan kernel path
+    lens = np.random.default_rng(rows).integers(0, 701, size=rows)
+    lens[::37] = 0  # some empty rows
+    cfg = synth.DecodeConfig("many", "bf16", rows=rows, n_heads=32, n_kv_heads=8, head_dim=128,
+                             block_size=16, ctx=("fixed", tuple(int(x) for x in lens)),
+                             pool=("factor", 1.5), max_ctx=704, seed=rows)
+    b = synth.make_batch(cfg, device=DEV)
+    sample = np.unique(np.concatenate([np.arange(6), np.arange(rows - 6, rows), [37, 74],
+                                       np.random.default_rng(1).choice(rows, 12, replace=False)]))
+    ref = oracle_read(b, sample)
+    got = gpu_read(b, out_dtype=torch.float32)[torch.as_tensor(sample, device=DEV)].cpu().numpy()
+    assert_close(got, ref, what="rows=%d" % rows, **TOL[torch.float32])
+    assert (b.ctx_host == 0).any()
