@@ -15,6 +15,7 @@ kernel timed with HIP events on the stream it runs on, and the CPU oracle
 timed on this host as a reported baseline.
 """
 import argparse
+import hashlib
 import json
 import os
 import sys
@@ -25,6 +26,29 @@ sys.path.insert(0, ROOT)
 
 METRIC = "paged decode read µs/call + achieved HBM GB/s (% peak), 8B-shaped layer"
 HBM_PEAK_GBS = 8000.0
+
+# HBM bytes per read measured with rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by
+# a plain copy of known size (profiles/decode_stream_<workload>_hbm_counters.md),
+# valid only for the kernel sources they were taken on.
+PROFILED_TRAFFIC = {
+    "llama3_8b_layer": {"src": "4b74aa1a38f4ddc6", "read_bytes": 587593026},
+}
+KERNEL_SOURCES = ("decode.hip", "pkv_internal.h", "abi.hip")
+
+
+def kernel_source_hash():
+    h = hashlib.sha256()
+    for f in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, "paged_kv_cache_13_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def profiled_traffic(workload):
+    rec = PROFILED_TRAFFIC.get(workload)
+    if rec is None or rec["src"] != kernel_source_hash():
+        return None
+    return rec["read_bytes"]
 
 
 def parse():
@@ -38,6 +62,9 @@ def parse():
                     help="extra reads timed with the 256 MB Infinity Cache flushed before each")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline (0 disables it)")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a plain 256 MiB device-to-device copy 5 times (a kernel of "
+                         "known traffic, to scale HBM counters by) and exit")
     return ap.parse_args()
 
 
@@ -97,6 +124,15 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.copy_calibration:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(5):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": src.numel() * 4,
+                          "copy_calibration_bytes_written": dst.numel() * 4, "calls": 5}))
+        return
     pkv.load_library()
     cfg = synth.CONFIGS[args.workload]
     batch = synth.make_batch(cfg, device=dev)
@@ -192,8 +228,10 @@ def main():
         "read_bytes": rb,
         "scatter_bytes": sb,
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": None,
-                     "kernel": "paged decode read (decode_partition + decode_merge)"},
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
+                     "traffic": profiled_traffic(cfg.name),
+                     "kernel": "paged decode read call (decode_stream + decode_stream_merge)",
+                     "bytes_per_launch": rb, "us_per_launch": round(read_us, 2)},
     }
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(batch, new_k, new_v, slots_h, args.cpu_seconds)
