@@ -51,7 +51,7 @@ __host__ __device__ inline WsLayout ws_layout(int32_t rows, int32_t n_heads, int
 //   gpre[rows + 1]         exclusive prefix of groups per row
 //   counters[kv * rows]    partial slices written per (kv head, row)
 //   partials[kv * rows * max_parts][slot]  fp32 acc[group][hd], m[group], l[group]
-constexpr int kStreamWaves = 2048;
+constexpr int kStreamWaves = 1024;  // one persistent wave per SIMD (4 per CU)
 constexpr int kWindowRows = 256;  // rows a wave keeps (and, if that is all, plans) in LDS
 constexpr int kPlanMaxRows = 8192;
 constexpr int kGroupPositions = 32;

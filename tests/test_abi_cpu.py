@@ -78,10 +78,10 @@ def test_workspace_size_partition_layout(lib):
 
 
 def test_workspace_size_stream_layout(lib):
-    # bf16, head_dim 128: header (4 words), 2048 wave starts (2 words each),
+    # bf16, head_dim 128: header (4 words), 1024 wave starts (2 words each),
     # 65 group prefixes, 8 x 64 row counters, aligned; then per (kv head, row)
     # 128 / 16 + 1 = 9 partial slots of align4(4 heads x 130) = 520 floats
-    head = 4 + 2 * 2048 + 65 + 8 * 64
+    head = 4 + 2 * 1024 + 65 + 8 * 64
     head += -head % 4
     assert ws(lib) == (head + 8 * 64 * 9 * 520) * 4
     # the stream layout always needs its header, even when no row can split
