@@ -62,6 +62,8 @@ def parse():
                     help="extra reads timed with the 256 MB Infinity Cache flushed before each")
     ap.add_argument("--cpu-seconds", type=float, default=10.0,
                     help="target CPU time of the oracle baseline (0 disables it)")
+    ap.add_argument("--headline-only", action="store_true",
+                    help="skip the other workloads (small fp32 reads, skewed batch, decode runs)")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (a kernel of "
                          "known traffic, to scale HBM counters by) and exit")
@@ -97,6 +99,97 @@ def cpu_baseline(batch, new_k, new_v, slots_h, budget_s):
             "sample": "the full workload (%d rows, sum ctx %d), %d step(s): scatter + read, "
                       "single-threaded C in fp64" % (cfg.rows, int(batch.ctx_host.sum()), reps),
             "cpu": cpu_model()}
+
+
+def _timed(fn, stream, calls, lead_cycles=200000):
+    """Mean and median µs of `calls` calls of fn, each bracketed by HIP events.
+    A short spin kernel runs before each call so that the host has enqueued
+    the events and the call before the GPU reaches them: the events then
+    measure GPU time only, not Python launch overhead."""
+    import numpy as np
+    import torch
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(calls)]
+    for a, b in ev:
+        torch.cuda._sleep(lead_cycles)
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    us = np.array([a.elapsed_time(b) for a, b in ev]) * 1e3
+    return float(us.mean()), float(np.median(us))
+
+
+def other_workloads(dev, stream):
+    """The remaining synthetic workloads: each read's µs and HBM rate, and the
+    decode-run sweep's per-step scatter / paged read / gathered-rectangle read."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_13_amd as pkv
+    from paged_kv_cache_13_amd import harness, synth
+
+    res = {}
+    for name, calls in (("tiny_f32", 100), ("gqa_f32", 100), ("skewed_long", 20)):
+        cfg = synth.CONFIGS[name]
+        b = synth.make_batch(cfg, device=dev)
+        out = torch.empty_like(b.q)
+        ws = torch.zeros(max(pkv.workspace_size(b.q, b.k_pool, b.block_table), 1), dtype=torch.uint8, device=dev)
+
+        def read():
+            pkv.paged_attention_into(b.q, b.k_pool, b.v_pool, b.block_table, b.context_lens, b.scale, out, ws)
+
+        for _ in range(5):
+            read()
+        mean, med = _timed(read, stream, calls)
+        e = 2 if cfg.dtype == "bf16" else 4
+        nb = harness.read_bytes(b.ctx_host, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.block_size, e, e)
+        res[name] = {"read_us": round(mean, 2), "read_us_median": round(med, 2), "read_bytes": nb,
+                     "GB/s": round(nb / (mean * 1e-6) / 1e9, 1),
+                     "pct_peak": round(100 * nb / (mean * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
+                     "sum_ctx": int(b.ctx_host.sum())}
+        del b, out, ws
+    runs = {}
+    for rows in (32, 128):
+        for bs in (8, 16, 32):
+            run = synth.DecodeRun(rows=rows, block_size=bs, prompt=512, steps=256, device=dev,
+                                  seed=5000 + rows + bs)
+            k, v, slots = run.prefill()
+            pre_us, _ = _timed(lambda: pkv.reshape_and_cache(k, v, slots, run.k_pool, run.v_pool), stream, 1,
+                               lead_cycles=2000000)
+            # every step's inputs are drawn first (host-side block allocation),
+            # so that the timed loop only enqueues GPU work
+            steps = []
+            for _ in range(run.steps):
+                q, kn, vn, sl = run.step()
+                bt, cl = run.block_table(), run.context_lens()
+                ws = torch.zeros(max(pkv.workspace_size(q, run.k_pool, bt), 1), dtype=torch.uint8, device=dev)
+                steps.append((q, kn, vn, sl, bt, cl, ws, run.ctx_host.copy()))
+            stats = harness.ReadStats("streamed", block=bs)
+            out = torch.empty(rows, run.n_heads, run.head_dim, dtype=torch.bfloat16, device=dev)
+            t_sc, t_rd, t_rect, rbytes = [], [], [], 0
+            for q, kn, vn, sl, bt, cl, ws, ctx in steps:
+                t_sc.append(_timed(lambda: pkv.reshape_and_cache(kn, vn, sl, run.k_pool, run.v_pool), stream, 1)[0])
+                t_rd.append(_timed(lambda: pkv.paged_attention_into(q, run.k_pool, run.v_pool, bt, cl, run.scale,
+                                                                     out, ws), stream, 1)[0])
+                t_rect.append(_timed(lambda: harness.gathered_rect_read(q, run.k_pool, run.v_pool, bt, cl,
+                                                                        run.scale), stream, 1,
+                                     lead_cycles=1000000)[0])
+                stats.record(rows, run.n_heads, 1, int(ctx.max()))
+                rbytes += harness.read_bytes(ctx, run.n_heads, run.n_kv_heads, run.head_dim, bs, 2, 2)
+            rd = float(np.mean(t_rd))
+            runs["rows%d_bs%d" % (rows, bs)] = {
+                "prefill_scatter_us": round(pre_us, 1),
+                "prefill_scatter_GB/s": round(harness.scatter_bytes(rows * run.prompt, run.n_kv_heads,
+                                                                    run.head_dim, 2) / (pre_us * 1e-6) / 1e9, 1),
+                "step_scatter_us": round(float(np.mean(t_sc)), 2), "step_read_us": round(rd, 2),
+                "step_read_GB/s": round(rbytes / run.steps / (rd * 1e-6) / 1e9, 1),
+                "step_rect_us": round(float(np.mean(t_rect)), 2),
+                "rect_over_paged": round(float(np.mean(t_rect)) / rd, 2),
+                "readstats": {"calls": stats.calls, "rows": stats.rows, "score_cells": stats.score_cells,
+                              "held_cells": stats.held_cells, "saving": round(stats.saving, 2)}}
+            del run, out, steps
+    res["decode_run"] = runs
+    return res
 
 
 def cpu_model():
@@ -235,6 +328,10 @@ def main():
     }
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(batch, new_k, new_v, slots_h, args.cpu_seconds)
+    if not args.headline_only:
+        del batch, out, ws, new_k, new_v
+        torch.cuda.empty_cache()
+        res["other_workloads"] = other_workloads(dev, stream)
     print(json.dumps(res), flush=True)
 
 

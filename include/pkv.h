@@ -86,9 +86,13 @@ typedef struct pkv_attn_desc {
   int64_t num_blocks;         /* blocks in each pool, >= 1 */
   int32_t dtype;              /* pkv_dtype of q, k_pool, v_pool */
   int32_t out_dtype;          /* pkv_dtype of out (normally == dtype) */
-  int32_t partition_tokens;   /* split-context partition length in positions:
-                                 0 = library default (512, at least one block);
-                                 else a positive multiple of block_size */
+  int32_t partition_tokens;   /* split-context partition length in positions,
+                                 a positive multiple of block_size, or 0 for the
+                                 library default: bf16 head_dim 64/128 reads cut
+                                 rows into slices of at least 128 positions;
+                                 other reads use partitions of at most 512
+                                 positions, shorter when rows x kv heads are
+                                 too few to fill the GPU */
 } pkv_attn_desc;
 
 /*

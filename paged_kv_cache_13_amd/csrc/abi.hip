@@ -13,6 +13,8 @@
 namespace {
 
 constexpr int32_t kDefaultPartition = 512;
+constexpr int64_t kTargetWorkgroups = 512;
+constexpr int32_t kStreamMinGroups = 4;  // 128 positions
 constexpr int32_t kMaxGroup = 16;
 constexpr int32_t kMaxPartitionBlocks = 4096;  // LDS holds one partition's block ids (16 KB)
 
@@ -31,6 +33,20 @@ int32_t log2i(int32_t x) {
 bool pool_fits(int64_t num_blocks, int32_t bs, int32_t n_kv, int32_t hd, int32_t dtype) {
   const int64_t per_block = (int64_t)bs * n_kv * hd * elem_bytes(dtype);
   return num_blocks >= 1 && num_blocks <= INT64_MAX / per_block;
+}
+
+// Default partition of the partition path: long enough to amortise a
+// workgroup (at most kDefaultPartition positions), short enough that the
+// grid of (partition, kv head, row) workgroups reaches kTargetWorkgroups
+// when rows are few.  From host shapes only.
+int32_t default_partition(const pkv_attn_desc *d, int32_t cap) {
+  const int64_t pairs = (int64_t)d->n_kv_heads * (d->rows > 0 ? d->rows : 1);
+  const int64_t want_parts = (kTargetWorkgroups + pairs - 1) / pairs;
+  int64_t part = (cap + want_parts - 1) / want_parts;
+  part = (part + d->block_size - 1) / d->block_size * d->block_size;
+  if (part > kDefaultPartition) part = kDefaultPartition;
+  if (part < d->block_size) part = d->block_size;
+  return (int32_t)part;
 }
 
 struct Plan {
@@ -54,7 +70,7 @@ int plan_decode(const pkv_attn_desc *d, Plan *pl) {
     return PKV_ERR_SHAPE;
   const int32_t cap = d->max_blocks_per_row * d->block_size;
   int32_t part = d->partition_tokens;
-  if (part == 0) part = kDefaultPartition;
+  if (part == 0) part = default_partition(d, cap);
   if (part < 0 || part % d->block_size != 0) return PKV_ERR_PARTITION;
   if (part > cap) part = cap;  // one partition covers every row: no split
   if (part / d->block_size > kMaxPartitionBlocks) return PKV_ERR_PARTITION;
@@ -70,7 +86,10 @@ int plan_decode(const pkv_attn_desc *d, Plan *pl) {
                d->rows <= pkv::kPlanMaxRows &&
                cap_groups * d->n_kv_heads * d->rows < (int64_t)INT_MAX;
   if (pl->stream) {
-    pl->cg_min = (part + pkv::kGroupPositions - 1) / pkv::kGroupPositions;
+    // slices of at least cg_min groups: the caller's partition length, else
+    // kStreamMinGroups, short enough that a small batch still fills every wave
+    pl->cg_min = d->partition_tokens ? (part + pkv::kGroupPositions - 1) / pkv::kGroupPositions
+                                     : kStreamMinGroups;
     pl->max_parts = (int32_t)((cap_groups + pl->cg_min - 1) / pl->cg_min + 1);
     if (d->rows > 0)
       pl->ws_bytes = pkv::stream_layout(d->rows, d->n_kv_heads, pl->group, d->head_dim, pl->max_parts).total *

@@ -1274,9 +1274,11 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
 
   bf16x8_t kc[2][KS], vc[DT];
   while (true) {
-    // the staged group is complete once every older load has returned; the
-    // block ids fetched after it may still be in flight
-    __builtin_amdgcn_s_waitcnt(0xF73);  // vmcnt(3)
+    // The staged group (and the next group's block ids) must have landed.
+    // The compiler does not order LDS reads after direct-to-LDS loads by
+    // itself, so the wait is explicit and fenced against reordering.
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -1284,6 +1286,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) vc[dt] = __builtin_bit_cast(bf16x8_t, s_v[dt * kWave + lane]);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the buffer may be refilled
+    asm volatile("" ::: "memory");
     const bool last_group = c0.idx + 1 >= total;
     GroupIds ids2;
     if (!last_group) {

@@ -80,10 +80,14 @@ def test_workspace_size_partition_layout(lib):
 def test_workspace_size_stream_layout(lib):
     # bf16, head_dim 128: header (4 words), 1024 wave starts (2 words each),
     # 65 group prefixes, 8 x 64 row counters, aligned; then per (kv head, row)
-    # 128 / 16 + 1 = 9 partial slots of align4(4 heads x 130) = 520 floats
+    # one partial slot of align4(4 heads x 130) = 520 floats per slice that can
+    # cut it: the default slices hold at least 4 groups of 32 positions, so
+    # 128 / 4 + 1 = 33 slots
     head = 4 + 2 * 1024 + 65 + 8 * 64
     head += -head % 4
-    assert ws(lib) == (head + 8 * 64 * 9 * 520) * 4
+    assert ws(lib) == (head + 8 * 64 * 33 * 520) * 4
+    # an explicit partition length sets the minimum slice: 512 -> 16 groups
+    assert ws(lib, partition_tokens=512) == (head + 8 * 64 * 9 * 520) * 4
     # the stream layout always needs its header, even when no row can split
     assert ws(lib, partition_tokens=4096) == (head + 8 * 64 * 2 * 520) * 4
     # more rows than the plan kernel scans: back to partitions

@@ -64,6 +64,49 @@ def test_scatter_is_bit_exact(dtype, hd, bs, nkv):
     assert torch.equal(vp_d.cpu().view(word), vp.view(word))
 
 
+@pytest.mark.parametrize("dtype,hd,bs,nkv,layout", [
+    ("bf16", 128, 16, 8, "prompt"), ("bf16", 128, 32, 8, "random"), ("bf16", 64, 8, 2, "prompt"),
+    ("f32", 128, 16, 8, "random"), ("f32", 16, 32, 1, "prompt"), ("bf16", 16, 8, 3, "random"),
+])
+def test_scatter_many_tokens_is_bit_exact(dtype, hd, bs, nkv, layout):
+    # 1061 tokens (a ragged last tile of 5) through the tiled scatter: prompt
+    # rows filling consecutive offsets, or a random slot permutation; padding
+    # and out-of-pool slots are skipped either way
+    note("scatter many %s hd=%d bs=%d nkv=%d %s" % (dtype, hd, bs, nkv, layout))
+    rng = np.random.default_rng(hd * 7 + bs + nkv)
+    T = 1061
+    nb = 2 * (T // bs + 8)
+    word = torch.int32 if dtype == "f32" else torch.int16
+    tdt = synth.torch_dtype(dtype)
+    g = torch.Generator().manual_seed(5)
+    bits = lambda shape: torch.randint(-2 ** 15, 2 ** 15, shape, generator=g, dtype=torch.int32).to(word)
+    k = bits((T, nkv, hd)).view(tdt)
+    v = bits((T, nkv, hd)).view(tdt)
+    if layout == "prompt":  # rows of 100 tokens, each row's blocks drawn from a shuffled free list
+        free = list(rng.permutation(nb))
+        slots = np.empty(T, dtype=np.int64)
+        for r0 in range(0, T, 100):
+            for pos in range(min(100, T - r0)):
+                if pos % bs == 0:
+                    blk = free.pop()
+                slots[r0 + pos] = blk * bs + pos % bs
+    else:
+        slots = rng.choice(nb * bs, size=T, replace=False).astype(np.int64)
+    slots[rng.choice(T, size=23, replace=False)] = -1
+    far = rng.choice(T, size=5, replace=False)
+    slots[far] = nb * bs + np.arange(5)  # outside the pool: skipped by the kernel
+    kp = bits((nb, nkv, bs, hd)).view(tdt)
+    vp = bits((nb, nkv, hd, bs)).view(tdt)
+    kp_d, vp_d = kp.to(DEV), vp.to(DEV)
+    pkv.reshape_and_cache(k.to(DEV), v.to(DEV), torch.from_numpy(slots).to(DEV), kp_d, vp_d)
+    torch.cuda.synchronize()
+    slots_o = slots.copy()
+    slots_o[far] = -1
+    oracle.reshape_and_cache(k, v, slots_o, kp, vp)
+    assert torch.equal(kp_d.cpu().view(word), kp.view(word))
+    assert torch.equal(vp_d.cpu().view(word), vp.view(word))
+
+
 def test_scatter_prefill_size_is_bit_exact():
     # a 128-row x 512-token prompt: 65536 tokens, 128 MiB of K + V
     run = synth.DecodeRun(rows=128, block_size=16, prompt=512, steps=0, device=DEV, seed=11)
@@ -171,23 +214,26 @@ def test_read_block_permutation_is_bitwise_invariant():
 
 @pytest.mark.parametrize("dtype,hd", [("bf16", 128), ("f32", 64)])
 def test_read_rows_are_independent(dtype, hd):
-    # permuting and padding the batch leaves every row's result in place (the
+    # permuting and padding the batch leaves every row's result in place.  The
     # bf16 path balances work over the whole batch, so where a row is split --
-    # and hence its last bits -- may move; the fp32 path splits per row)
+    # and hence its last bits -- may move; so does the default partition
+    # length of the fp32 path, which shrinks when rows are few.  With a fixed
+    # partition length the fp32 path splits every row the same way: bitwise.
     cfg = small_cfg(dtype, rows=6, H=32, KV=8, hd=hd, bs=16, lo=1, hi=2000, seed=3)
     b = synth.make_batch(cfg, device=DEV)
-    base = gpu_read(b, out_dtype=torch.float32)
     order = torch.tensor([5, 3, 1, 0, 2, 4, 0, 1], device=DEV)  # permuted and padded
     b2 = synth.DecodeBatch(**{**b.__dict__})
     b2.q = b.q[order].contiguous()
     b2.block_table = b.block_table[order].contiguous()
     b2.context_lens = b.context_lens[order].contiguous()
     b2.cfg = cfg.replace(rows=8)
+    base = gpu_read(b, out_dtype=torch.float32)
     got = gpu_read(b2, out_dtype=torch.float32)
+    assert_close(got.cpu(), base[order].cpu(), what="rows", atol=2e-6, rtol=1e-5)
     if dtype == "f32":
+        base = gpu_read(b, out_dtype=torch.float32, partition=256)
+        got = gpu_read(b2, out_dtype=torch.float32, partition=256)
         assert torch.equal(base[order], got)
-    else:
-        assert_close(got.cpu(), base[order].cpu(), what="rows", atol=2e-6, rtol=1e-5)
 
 
 @pytest.mark.parametrize("name", ["llama3_8b_layer", "skewed_long"])
