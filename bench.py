@@ -164,7 +164,7 @@ def other_workloads(dev, stream):
                 bt, cl = run.block_table(), run.context_lens()
                 ws = torch.zeros(max(pkv.workspace_size(q, run.k_pool, bt), 1), dtype=torch.uint8, device=dev)
                 steps.append((q, kn, vn, sl, bt, cl, ws, run.ctx_host.copy()))
-            stats = harness.ReadStats("streamed", block=bs)
+            stats = pkv.ReadCounters("streamed", block=bs)
             out = torch.empty(rows, run.n_heads, run.head_dim, dtype=torch.bfloat16, device=dev)
             t_sc, t_rd, t_rect, rbytes = [], [], [], 0
             for q, kn, vn, sl, bt, cl, ws, ctx in steps:
@@ -290,7 +290,7 @@ def main():
     ms_step = wall * 1e3 / K
     read_us = float(read_ms.mean() * 1e3)
     achieved = rb / (read_us * 1e-6) / 1e9
-    stats = harness.ReadStats("streamed", block=bs)
+    stats = pkv.ReadCounters("streamed", block=bs)
     stats.record(cfg.rows, cfg.n_heads, 1, int(batch.ctx_host.max()))
     print("readstats: mode=%s block=%d calls=%d rows=%d score_cells=%d held_cells=%d saving=%.1fx"
           % (stats.mode, stats.block, stats.calls, stats.rows, stats.score_cells, stats.held_cells,

@@ -67,7 +67,8 @@ typedef enum pkv_status {
   PKV_ERR_SHAPE = 7,         /* a size is negative, zero where it may not be, or overflows */
   PKV_ERR_WORKSPACE = 8,     /* workspace NULL or smaller than pkv_paged_attention_workspace_size */
   PKV_ERR_PARTITION = 9,     /* partition_tokens not a positive multiple of block_size */
-  PKV_ERR_LAUNCH = 10        /* the HIP runtime refused a launch (hipGetLastError) */
+  PKV_ERR_LAUNCH = 10,       /* the HIP runtime refused a launch (hipGetLastError) */
+  PKV_ERR_MODE = 11          /* read counters of different reads (mode or block differ) */
 } pkv_status;
 
 typedef enum pkv_dtype {
@@ -156,6 +157,68 @@ int pkv_paged_attention(const pkv_attn_desc *d, const void *q, const void *k_poo
  * sum.  0 when no row can span more than one partition.  Returns 0 for a
  * NULL descriptor. */
 size_t pkv_paged_attention_workspace_size(const pkv_attn_desc *d);
+
+/*
+ * pkv_decode_step -- one decode step of every row: append the step's new
+ * token, then read.  ("Day 60" page, "Tomorrow": with the streamed read a
+ * decode step presents a shape of rows and nothing else.)
+ *
+ * Equivalent to pkv_reshape_and_cache(k_new, v_new, slot_mapping, d->rows,
+ * ...) followed by pkv_paged_attention(d, q, ...), enqueued on `stream` in
+ * that order, after every check of both has passed (a refused call enqueues
+ * nothing).  The new token of row r is counted in context_lens[r] and lives
+ * at slot_mapping[r].  The kernels' launch shapes depend on the descriptor
+ * only (rows, heads, head_dim, block size, table width), never on lengths or
+ * block ids, so a captured graph of this call replays for any lengths.
+ *
+ *   k_new, v_new  device [rows, n_kv_heads, head_dim] of d->dtype
+ *   slot_mapping  device [rows] int64 (negative: no token this step)
+ *   other arguments as for pkv_paged_attention (k_pool, v_pool written)
+ */
+int pkv_decode_step(const pkv_attn_desc *d, const void *k_new, const void *v_new,
+                    const int64_t *slot_mapping, const void *q, void *k_pool, void *v_pool,
+                    const int32_t *block_table, const int32_t *context_lens, float scale, void *out,
+                    void *workspace, size_t workspace_bytes, void *stream);
+
+/*
+ * Read counters, kept by the caller for the read it runs ("Day 60" page,
+ * "What I added today": calls, rows, score cells, held cells and their
+ * quotient; "Why it matters": the cells come from shapes, so counting costs
+ * no device synchronisation; "What I learned", item 3: a window between two
+ * readings of different reads is refused).  Host arithmetic only.
+ *
+ * A read of `rows` rows, `heads` query heads and `query_len` queries per row
+ * over a context `width` positions wide is charged rows*heads*query_len*width
+ * score cells (the [rows, heads, query_len, width] rectangle).  The gathered
+ * read holds them all; the streamed read holds one tile of min(block, width)
+ * positions per (row, head, query).
+ */
+typedef enum pkv_read_mode {
+  PKV_READ_GATHERED = 0,      /* materialises the score rectangle */
+  PKV_READ_STREAMED = 1       /* walks tiles of `block` positions */
+} pkv_read_mode;
+
+typedef struct pkv_read_stats {
+  int32_t mode;               /* pkv_read_mode */
+  int32_t block;              /* tile width of a streamed read, >= 1 */
+  int64_t calls, rows, score_cells, held_cells;
+} pkv_read_stats;
+
+/* Zero the counters of a read of `mode` and tile width `block` (>= 1). */
+int pkv_read_stats_init(pkv_read_stats *s, int32_t mode, int32_t block);
+/* Count one read of the given shape (all >= 0); PKV_ERR_SHAPE on overflow. */
+int pkv_read_stats_record(pkv_read_stats *s, int32_t rows, int32_t heads, int32_t query_len,
+                          int32_t width);
+/* Count one pkv_paged_attention call of descriptor d: one query per row, the
+ * table's width max_blocks_per_row * block_size as the context width. */
+int pkv_read_stats_record_read(pkv_read_stats *s, const pkv_attn_desc *d);
+/* window = now - earlier; PKV_ERR_MODE if the two readings are of reads with
+ * a different mode or block, PKV_ERR_SHAPE if `earlier` is not earlier. */
+int pkv_read_stats_since(const pkv_read_stats *now, const pkv_read_stats *earlier,
+                         pkv_read_stats *window);
+/* score_cells / held_cells; 1.0 when nothing is held (the gathered read
+ * holds everything it is charged: its saving is 1, not "unmeasured"). */
+double pkv_read_stats_saving(const pkv_read_stats *s);
 
 /* Static text for a status code ("unknown status" for anything else). */
 const char *pkv_strerror(int status);

@@ -40,6 +40,14 @@ class AttnDesc(ctypes.Structure):
                 ("out_dtype", ctypes.c_int32), ("partition_tokens", ctypes.c_int32)]
 
 
+class ReadStatsStruct(ctypes.Structure):
+    _fields_ = [("mode", ctypes.c_int32), ("block", ctypes.c_int32), ("calls", ctypes.c_int64),
+                ("rows", ctypes.c_int64), ("score_cells", ctypes.c_int64), ("held_cells", ctypes.c_int64)]
+
+
+_MODES = {"gathered": 0, "streamed": 1}
+
+
 def library_path() -> str:
     return _LIB_PATH
 
@@ -65,6 +73,20 @@ def load_library():
     lib.pkv_strerror.restype = ctypes.c_char_p
     lib.pkv_version.argtypes = []
     lib.pkv_version.restype = ctypes.c_int
+    lib.pkv_decode_step.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp,
+                                    ctypes.c_float, vp, vp, sz, vp]
+    lib.pkv_decode_step.restype = ctypes.c_int
+    rs = ctypes.POINTER(ReadStatsStruct)
+    lib.pkv_read_stats_init.argtypes = [rs, i32, i32]
+    lib.pkv_read_stats_init.restype = ctypes.c_int
+    lib.pkv_read_stats_record.argtypes = [rs, i32, i32, i32, i32]
+    lib.pkv_read_stats_record.restype = ctypes.c_int
+    lib.pkv_read_stats_record_read.argtypes = [rs, ctypes.POINTER(AttnDesc)]
+    lib.pkv_read_stats_record_read.restype = ctypes.c_int
+    lib.pkv_read_stats_since.argtypes = [rs, rs, rs]
+    lib.pkv_read_stats_since.restype = ctypes.c_int
+    lib.pkv_read_stats_saving.argtypes = [rs]
+    lib.pkv_read_stats_saving.restype = ctypes.c_double
     _lib = lib
     return lib
 
@@ -145,12 +167,7 @@ def workspace_size(q: torch.Tensor, k_pool: torch.Tensor, block_table: torch.Ten
     return int(load_library().pkv_paged_attention_workspace_size(ctypes.byref(d)))
 
 
-def paged_attention_into(q, k_pool, v_pool, block_table, context_lens, scale, out,
-                         workspace: Optional[torch.Tensor] = None,
-                         partition_tokens: int = 0) -> torch.Tensor:
-    """Paged decode read into a caller-provided `out` [rows, n_heads, hd]
-    (float32 or bfloat16).  `workspace` is a uint8 GPU tensor; when None one of
-    the required size is allocated by torch for this call."""
+def _read_args(q, k_pool, v_pool, block_table, context_lens, out, workspace, partition_tokens):
     dev = _on_gpu(q, k_pool, v_pool, block_table, context_lens, out)
     _require(q.dim() == 3, "q must be [rows, n_heads, head_dim]")
     _check_pools(k_pool, v_pool)
@@ -161,25 +178,110 @@ def paged_attention_into(q, k_pool, v_pool, block_table, context_lens, scale, ou
              "context_lens must be int32 [rows]")
     _require(out.shape == q.shape, "out must be [rows, n_heads, head_dim]")
     d = _desc(q, k_pool, block_table, _dtype_code(out), partition_tokens)
-    lib = load_library()
-    need = int(lib.pkv_paged_attention_workspace_size(ctypes.byref(d)))
+    need = int(load_library().pkv_paged_attention_workspace_size(ctypes.byref(d)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
     else:
         _on_gpu(workspace)
-    _check(lib.pkv_paged_attention(
+    wsp = workspace.data_ptr() if need else None
+    return dev, d, wsp, workspace.numel() * workspace.element_size()
+
+
+def paged_attention_into(q, k_pool, v_pool, block_table, context_lens, scale, out,
+                         workspace: Optional[torch.Tensor] = None,
+                         partition_tokens: int = 0, stats: Optional["ReadCounters"] = None) -> torch.Tensor:
+    """Paged decode read into a caller-provided `out` [rows, n_heads, hd]
+    (float32 or bfloat16).  `workspace` is a uint8 GPU tensor; when None one of
+    the required size is allocated by torch for this call.  `stats`, if
+    given, counts the call (host arithmetic from shapes)."""
+    dev, d, wsp, wsb = _read_args(q, k_pool, v_pool, block_table, context_lens, out, workspace,
+                                  partition_tokens)
+    _check(load_library().pkv_paged_attention(
         ctypes.byref(d), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(),
         block_table.data_ptr(), context_lens.data_ptr(), ctypes.c_float(scale), out.data_ptr(),
-        workspace.data_ptr() if need else None, workspace.numel() * workspace.element_size(),
-        _stream_handle(dev)))
+        wsp, wsb, _stream_handle(dev)))
+    if stats is not None:
+        stats.record_read(d)
     return out
 
 
+def decode_step(q, k_new, v_new, slot_mapping, k_pool, v_pool, block_table, context_lens, scale,
+                out=None, workspace: Optional[torch.Tensor] = None, partition_tokens: int = 0,
+                stats: Optional["ReadCounters"] = None) -> torch.Tensor:
+    """One decode step of every row: scatter k_new, v_new [rows, n_kv, hd] to
+    slot_mapping [rows] (int64), then the paged read of q -- one library call,
+    two kernels on the current stream, no host synchronisation."""
+    if out is None:
+        out = torch.empty_like(q)
+    dev, d, wsp, wsb = _read_args(q, k_pool, v_pool, block_table, context_lens, out, workspace,
+                                  partition_tokens)
+    _on_gpu(k_new, v_new, slot_mapping, q)
+    _require(k_new.dim() == 3 and v_new.shape == k_new.shape and k_new.shape[0] == q.shape[0]
+             and k_new.shape[1] == k_pool.shape[1] and k_new.shape[2] == k_pool.shape[3],
+             "k_new, v_new must be [rows, n_kv_heads, head_dim]")
+    _require(k_new.dtype == q.dtype and v_new.dtype == q.dtype, "k_new, v_new must have q's dtype")
+    _require(slot_mapping.dtype == torch.int64 and slot_mapping.shape == (q.shape[0],),
+             "slot_mapping must be int64 [rows]")
+    _check(load_library().pkv_decode_step(
+        ctypes.byref(d), k_new.data_ptr(), v_new.data_ptr(), slot_mapping.data_ptr(), q.data_ptr(),
+        k_pool.data_ptr(), v_pool.data_ptr(), block_table.data_ptr(), context_lens.data_ptr(),
+        ctypes.c_float(scale), out.data_ptr(), wsp, wsb, _stream_handle(dev)))
+    if stats is not None:
+        stats.record_read(d)
+    return out
+
+
+class ReadCounters:
+    """The library's read counters (pkv_read_stats): calls, rows, score cells
+    a [rows, heads, query_len, width] rectangle is charged, cells the read
+    holds, and their quotient.  Host arithmetic only."""
+
+    def __init__(self, mode: str = "streamed", block: int = 16):
+        self._s = ReadStatsStruct()
+        _check(load_library().pkv_read_stats_init(ctypes.byref(self._s), _MODES[mode], int(block)))
+
+    @classmethod
+    def _wrap(cls, st: ReadStatsStruct) -> "ReadCounters":
+        obj = cls.__new__(cls)
+        obj._s = st
+        return obj
+
+    def record(self, rows: int, heads: int, query_len: int, width: int) -> None:
+        _check(load_library().pkv_read_stats_record(ctypes.byref(self._s), rows, heads, query_len, width))
+
+    def record_read(self, desc: AttnDesc) -> None:
+        _check(load_library().pkv_read_stats_record_read(ctypes.byref(self._s), ctypes.byref(desc)))
+
+    def snapshot(self) -> "ReadCounters":
+        st = ReadStatsStruct()
+        ctypes.memmove(ctypes.byref(st), ctypes.byref(self._s), ctypes.sizeof(st))
+        return ReadCounters._wrap(st)
+
+    def since(self, earlier: "ReadCounters") -> "ReadCounters":
+        """The window between an earlier reading and this one; a reading of
+        another read (mode or block differ) is refused."""
+        out = ReadStatsStruct()
+        _check(load_library().pkv_read_stats_since(ctypes.byref(self._s), ctypes.byref(earlier._s),
+                                                    ctypes.byref(out)))
+        return ReadCounters._wrap(out)
+
+    mode = property(lambda self: {v: k for k, v in _MODES.items()}[self._s.mode])
+    block = property(lambda self: self._s.block)
+    calls = property(lambda self: self._s.calls)
+    rows = property(lambda self: self._s.rows)
+    score_cells = property(lambda self: self._s.score_cells)
+    held_cells = property(lambda self: self._s.held_cells)
+
+    @property
+    def saving(self) -> float:
+        return float(load_library().pkv_read_stats_saving(ctypes.byref(self._s)))
+
+
 def paged_attention(q, k_pool, v_pool, block_table, context_lens, scale, out=None,
-                    partition_tokens: int = 0) -> torch.Tensor:
+                    partition_tokens: int = 0, stats: Optional[ReadCounters] = None) -> torch.Tensor:
     """nanoserve-style call: returns attention output [rows, n_heads, head_dim]
     in q's dtype (or writes `out` if given)."""
     if out is None:
         out = torch.empty_like(q)
     return paged_attention_into(q, k_pool, v_pool, block_table, context_lens, scale, out,
-                                partition_tokens=partition_tokens)
+                                partition_tokens=partition_tokens, stats=stats)

@@ -106,71 +106,30 @@ int plan_decode(const pkv_attn_desc *d, Plan *pl) {
   return PKV_OK;
 }
 
-}  // namespace
+int check_scatter(const void *k, const void *v, const int64_t *slot_mapping, int64_t num_tokens,
+                  const void *k_pool, const void *v_pool, int64_t num_blocks, int32_t block_size,
+                  int32_t n_kv_heads, int32_t head_dim, int32_t dtype);
 
-extern "C" {
-
-int pkv_version(void) { return 100; }
-
-const char *pkv_strerror(int status) {
-  switch (status) {
-    case PKV_OK: return "ok";
-    case PKV_ERR_NULL: return "a required pointer is NULL";
-    case PKV_ERR_ALIGN: return "a buffer is not aligned (16 bytes for K/V/q/out/workspace)";
-    case PKV_ERR_DTYPE: return "unsupported dtype (0 = f32, 1 = bf16)";
-    case PKV_ERR_HEADS: return "n_heads must be a multiple of n_kv_heads with group <= 16";
-    case PKV_ERR_HEAD_DIM: return "head_dim must be 16, 64 or 128";
-    case PKV_ERR_BLOCK_SIZE: return "block_size must be 8, 16 or 32";
-    case PKV_ERR_SHAPE: return "a size is out of range or overflows";
-    case PKV_ERR_WORKSPACE: return "workspace missing or smaller than pkv_paged_attention_workspace_size";
-    case PKV_ERR_PARTITION: return "partition_tokens must be a positive multiple of block_size";
-    case PKV_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
-    default: return "unknown status";
-  }
-}
-
-int pkv_reshape_and_cache(const void *k, const void *v, const int64_t *slot_mapping,
-                          int64_t num_tokens, void *k_pool, void *v_pool, int64_t num_blocks,
-                          int32_t block_size, int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
-                          void *stream) {
-  if (!k || !v || !slot_mapping || !k_pool || !v_pool) return PKV_ERR_NULL;
-  if (!dtype_ok(dtype)) return PKV_ERR_DTYPE;
-  if (!head_dim_ok(head_dim)) return PKV_ERR_HEAD_DIM;
-  if (!block_size_ok(block_size)) return PKV_ERR_BLOCK_SIZE;
-  if (num_tokens < 0 || num_tokens > INT_MAX || n_kv_heads < 1 || n_kv_heads > 4096)
-    return PKV_ERR_SHAPE;
-  if (!pool_fits(num_blocks, block_size, n_kv_heads, head_dim, dtype)) return PKV_ERR_SHAPE;
-  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
-      !aligned(slot_mapping, 8))
-    return PKV_ERR_ALIGN;
-  if (num_tokens == 0) return PKV_OK;
-  const hipError_t e = pkv::launch_scatter(k, v, slot_mapping, num_tokens, k_pool, v_pool,
-                                           num_blocks, block_size, n_kv_heads, head_dim, dtype,
-                                           static_cast<hipStream_t>(stream));
-  return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
-}
-
-size_t pkv_paged_attention_workspace_size(const pkv_attn_desc *d) {
-  Plan pl;
-  if (plan_decode(d, &pl) != PKV_OK) return 0;
-  return pl.ws_bytes;
-}
-
-int pkv_paged_attention(const pkv_attn_desc *d, const void *q, const void *k_pool,
-                        const void *v_pool, const int32_t *block_table,
-                        const int32_t *context_lens, float scale, void *out, void *workspace,
-                        size_t workspace_bytes, void *stream) {
-  Plan pl;
-  const int st = plan_decode(d, &pl);
+// Every host-side check of a read, before anything is enqueued.
+int check_attention(const pkv_attn_desc *d, const void *q, const void *k_pool, const void *v_pool,
+                    const int32_t *block_table, const int32_t *context_lens, const void *out,
+                    const void *workspace, size_t workspace_bytes, Plan *pl) {
+  const int st = plan_decode(d, pl);
   if (st != PKV_OK) return st;
   if (!q || !k_pool || !v_pool || !block_table || !context_lens || !out) return PKV_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16) ||
       !aligned(block_table, 4) || !aligned(context_lens, 4))
     return PKV_ERR_ALIGN;
-  if (pl.ws_bytes > 0) {
-    if (!workspace || workspace_bytes < pl.ws_bytes) return PKV_ERR_WORKSPACE;
+  if (pl->ws_bytes > 0) {
+    if (!workspace || workspace_bytes < pl->ws_bytes) return PKV_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return PKV_ERR_ALIGN;
   }
+  return PKV_OK;
+}
+
+int launch_attention(const pkv_attn_desc *d, const Plan &pl, const void *q, const void *k_pool,
+                     const void *v_pool, const int32_t *block_table, const int32_t *context_lens,
+                     float scale, void *out, void *workspace, hipStream_t stream) {
   if (d->rows == 0) return PKV_OK;
   pkv::DecodeArgs a;
   a.q = q;
@@ -197,8 +156,161 @@ int pkv_paged_attention(const pkv_attn_desc *d, const void *q, const void *k_poo
   a.dtype = d->dtype;
   a.out_dtype = d->out_dtype;
   a.scale = scale;
-  const hipError_t e = pkv::launch_decode(a, static_cast<hipStream_t>(stream));
+  return pkv::launch_decode(a, stream) == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_version(void) { return 200; }
+
+const char *pkv_strerror(int status) {
+  switch (status) {
+    case PKV_OK: return "ok";
+    case PKV_ERR_NULL: return "a required pointer is NULL";
+    case PKV_ERR_ALIGN: return "a buffer is not aligned (16 bytes for K/V/q/out/workspace)";
+    case PKV_ERR_DTYPE: return "unsupported dtype (0 = f32, 1 = bf16)";
+    case PKV_ERR_HEADS: return "n_heads must be a multiple of n_kv_heads with group <= 16";
+    case PKV_ERR_HEAD_DIM: return "head_dim must be 16, 64 or 128";
+    case PKV_ERR_BLOCK_SIZE: return "block_size must be 8, 16 or 32";
+    case PKV_ERR_SHAPE: return "a size is out of range or overflows";
+    case PKV_ERR_WORKSPACE: return "workspace missing or smaller than pkv_paged_attention_workspace_size";
+    case PKV_ERR_PARTITION: return "partition_tokens must be a positive multiple of block_size";
+    case PKV_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
+    case PKV_ERR_MODE: return "read counters of different reads (mode or block differ)";
+    default: return "unknown status";
+  }
+}
+
+int pkv_reshape_and_cache(const void *k, const void *v, const int64_t *slot_mapping,
+                          int64_t num_tokens, void *k_pool, void *v_pool, int64_t num_blocks,
+                          int32_t block_size, int32_t n_kv_heads, int32_t head_dim, int32_t dtype,
+                          void *stream) {
+  const int st = check_scatter(k, v, slot_mapping, num_tokens, k_pool, v_pool, num_blocks, block_size,
+                               n_kv_heads, head_dim, dtype);
+  if (st != PKV_OK) return st;
+  if (num_tokens == 0) return PKV_OK;
+  const hipError_t e = pkv::launch_scatter(k, v, slot_mapping, num_tokens, k_pool, v_pool,
+                                           num_blocks, block_size, n_kv_heads, head_dim, dtype,
+                                           static_cast<hipStream_t>(stream));
   return e == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+}
+
+}  // extern "C"
+
+namespace {
+
+int check_scatter(const void *k, const void *v, const int64_t *slot_mapping, int64_t num_tokens,
+                  const void *k_pool, const void *v_pool, int64_t num_blocks, int32_t block_size,
+                  int32_t n_kv_heads, int32_t head_dim, int32_t dtype) {
+  if (!k || !v || !slot_mapping || !k_pool || !v_pool) return PKV_ERR_NULL;
+  if (!dtype_ok(dtype)) return PKV_ERR_DTYPE;
+  if (!head_dim_ok(head_dim)) return PKV_ERR_HEAD_DIM;
+  if (!block_size_ok(block_size)) return PKV_ERR_BLOCK_SIZE;
+  if (num_tokens < 0 || num_tokens > INT_MAX || n_kv_heads < 1 || n_kv_heads > 4096)
+    return PKV_ERR_SHAPE;
+  if (!pool_fits(num_blocks, block_size, n_kv_heads, head_dim, dtype)) return PKV_ERR_SHAPE;
+  if (!aligned(k, 16) || !aligned(v, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) ||
+      !aligned(slot_mapping, 8))
+    return PKV_ERR_ALIGN;
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t pkv_paged_attention_workspace_size(const pkv_attn_desc *d) {
+  Plan pl;
+  if (plan_decode(d, &pl) != PKV_OK) return 0;
+  return pl.ws_bytes;
+}
+
+int pkv_paged_attention(const pkv_attn_desc *d, const void *q, const void *k_pool,
+                        const void *v_pool, const int32_t *block_table,
+                        const int32_t *context_lens, float scale, void *out, void *workspace,
+                        size_t workspace_bytes, void *stream) {
+  Plan pl;
+  const int st = check_attention(d, q, k_pool, v_pool, block_table, context_lens, out, workspace,
+                                 workspace_bytes, &pl);
+  if (st != PKV_OK) return st;
+  return launch_attention(d, pl, q, k_pool, v_pool, block_table, context_lens, scale, out, workspace,
+                          static_cast<hipStream_t>(stream));
+}
+
+int pkv_decode_step(const pkv_attn_desc *d, const void *k_new, const void *v_new,
+                    const int64_t *slot_mapping, const void *q, void *k_pool, void *v_pool,
+                    const int32_t *block_table, const int32_t *context_lens, float scale, void *out,
+                    void *workspace, size_t workspace_bytes, void *stream) {
+  Plan pl;
+  int st = check_attention(d, q, k_pool, v_pool, block_table, context_lens, out, workspace,
+                           workspace_bytes, &pl);
+  if (st != PKV_OK) return st;
+  st = check_scatter(k_new, v_new, slot_mapping, d->rows, k_pool, v_pool, d->num_blocks, d->block_size,
+                     d->n_kv_heads, d->head_dim, d->dtype);
+  if (st != PKV_OK) return st;
+  if (d->rows == 0) return PKV_OK;
+  const hipStream_t hs = static_cast<hipStream_t>(stream);
+  if (pkv::launch_scatter(k_new, v_new, slot_mapping, d->rows, k_pool, v_pool, d->num_blocks,
+                          d->block_size, d->n_kv_heads, d->head_dim, d->dtype, hs) != hipSuccess)
+    return PKV_ERR_LAUNCH;
+  return launch_attention(d, pl, q, k_pool, v_pool, block_table, context_lens, scale, out, workspace, hs);
+}
+
+int pkv_read_stats_init(pkv_read_stats *s, int32_t mode, int32_t block) {
+  if (!s) return PKV_ERR_NULL;
+  if ((mode != PKV_READ_GATHERED && mode != PKV_READ_STREAMED) || block < 1) return PKV_ERR_SHAPE;
+  s->mode = mode;
+  s->block = block;
+  s->calls = s->rows = s->score_cells = s->held_cells = 0;
+  return PKV_OK;
+}
+
+int pkv_read_stats_record(pkv_read_stats *s, int32_t rows, int32_t heads, int32_t query_len, int32_t width) {
+  if (!s) return PKV_ERR_NULL;
+  if (rows < 0 || heads < 0 || query_len < 0 || width < 0) return PKV_ERR_SHAPE;
+  // rows * heads * query_len <= 2^93 in theory: bound each product in 63 bits
+  const int64_t lanes = (int64_t)rows * heads;
+  if (query_len && lanes > INT64_MAX / query_len) return PKV_ERR_SHAPE;
+  const int64_t q = lanes * query_len;
+  if (width && q > INT64_MAX / width) return PKV_ERR_SHAPE;
+  const int64_t cells = q * width;
+  const int64_t held = s->mode == PKV_READ_STREAMED ? q * (width < s->block ? width : s->block) : cells;
+  if (s->score_cells > INT64_MAX - cells || s->held_cells > INT64_MAX - held) return PKV_ERR_SHAPE;
+  s->calls += 1;
+  s->rows += rows;
+  s->score_cells += cells;
+  s->held_cells += held;
+  return PKV_OK;
+}
+
+int pkv_read_stats_record_read(pkv_read_stats *s, const pkv_attn_desc *d) {
+  if (!s || !d) return PKV_ERR_NULL;
+  if (d->rows < 0 || d->n_heads < 1 || d->max_blocks_per_row < 1 || d->block_size < 1 ||
+      (int64_t)d->max_blocks_per_row * d->block_size > INT_MAX)
+    return PKV_ERR_SHAPE;
+  return pkv_read_stats_record(s, d->rows, d->n_heads, 1, d->max_blocks_per_row * d->block_size);
+}
+
+int pkv_read_stats_since(const pkv_read_stats *now, const pkv_read_stats *earlier, pkv_read_stats *window) {
+  if (!now || !earlier || !window) return PKV_ERR_NULL;
+  if (now->mode != earlier->mode || now->block != earlier->block) return PKV_ERR_MODE;
+  if (now->calls < earlier->calls || now->rows < earlier->rows || now->score_cells < earlier->score_cells ||
+      now->held_cells < earlier->held_cells)
+    return PKV_ERR_SHAPE;  // not an earlier reading of the same counters
+  window->mode = now->mode;
+  window->block = now->block;
+  window->calls = now->calls - earlier->calls;
+  window->rows = now->rows - earlier->rows;
+  window->score_cells = now->score_cells - earlier->score_cells;
+  window->held_cells = now->held_cells - earlier->held_cells;
+  return PKV_OK;
+}
+
+double pkv_read_stats_saving(const pkv_read_stats *s) {
+  if (!s || s->held_cells <= 0) return 1.0;
+  return (double)s->score_cells / (double)s->held_cells;
 }
 
 }  // extern "C"

@@ -7,13 +7,8 @@
   comparison arm of the decode-run sweep, never the product path.
 * ``read_bytes`` / ``scatter_bytes``: algorithmic HBM bytes of one call, from
   host-known shapes and lengths.
-* ``ReadStats``: cell accounting in the pages' terms (nanoserve "Day 60" page,
-  "What I added today" and "Why it matters": calls, rows, score cells a
-  rectangle read is charged, cells a streamed read holds, their quotient).
 """
 from __future__ import annotations
-
-import dataclasses
 
 import numpy as np
 import torch
@@ -73,43 +68,3 @@ def read_flops(ctx: np.ndarray, n_heads: int, head_dim: int) -> int:
 def scatter_bytes(tokens: int, n_kv: int, head_dim: int, elem: int) -> int:
     """K and V rows read and written once each, plus the int64 slot ids."""
     return 4 * tokens * n_kv * head_dim * elem + 8 * tokens
-
-
-@dataclasses.dataclass
-class ReadStats:
-    """Cells of one read mode, priced from shapes only (no device values).
-
-    charged: cells a [rows, heads, query_len, width] rectangle would hold;
-    held: cells the read holds -- the whole rectangle for the gathered read,
-    one tile of min(block, width) positions per (row, head) for the streamed
-    read.  saving = charged / held (1.0 for the rectangle).
-    """
-    mode: str
-    block: int = 0
-    calls: int = 0
-    rows: int = 0
-    score_cells: int = 0
-    held_cells: int = 0
-
-    def record(self, rows: int, heads: int, query_len: int, width: int) -> None:
-        cells = rows * heads * query_len * width
-        self.calls += 1
-        self.rows += rows
-        self.score_cells += cells
-        if self.mode == "streamed":
-            self.held_cells += rows * heads * query_len * min(self.block, width)
-        else:
-            self.held_cells += cells
-
-    @property
-    def saving(self) -> float:
-        return self.score_cells / self.held_cells if self.held_cells else 1.0
-
-    def since(self, earlier: "ReadStats") -> "ReadStats":
-        """The window between two readings of the same read."""
-        if earlier.mode != self.mode or earlier.block != self.block:
-            raise ValueError("readings of different reads (%s/%d vs %s/%d)"
-                             % (earlier.mode, earlier.block, self.mode, self.block))
-        return ReadStats(self.mode, self.block, self.calls - earlier.calls,
-                         self.rows - earlier.rows, self.score_cells - earlier.score_cells,
-                         self.held_cells - earlier.held_cells)

@@ -29,8 +29,11 @@ def declared_functions():
     return sorted(set(re.findall(r"\b(pkv_[a-z_]+)\s*\(", text)))
 
 
-def test_header_declares_the_five_entry_points():
-    assert declared_functions() == ["pkv_paged_attention", "pkv_paged_attention_workspace_size",
+def test_header_declares_the_entry_points():
+    assert declared_functions() == ["pkv_decode_step", "pkv_paged_attention",
+                                    "pkv_paged_attention_workspace_size", "pkv_read_stats_init",
+                                    "pkv_read_stats_record", "pkv_read_stats_record_read",
+                                    "pkv_read_stats_saving", "pkv_read_stats_since",
                                     "pkv_reshape_and_cache", "pkv_strerror", "pkv_version"]
 
 
@@ -40,11 +43,11 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, 11):
-        assert lib.pkv_strerror(code).decode()
+    for code in range(0, 12):
+        assert lib.pkv_strerror(code).decode() != "unknown status"
     assert lib.pkv_strerror(0).decode() == "ok"
     assert lib.pkv_strerror(999).decode() == "unknown status"
-    assert lib.pkv_version() == 100
+    assert lib.pkv_version() == 200
 
 
 def desc(**kw):
@@ -144,3 +147,79 @@ def test_scatter_refusals(lib):
     assert scatter(lib, k=FAKE + 4) == 2
     assert scatter(lib, sm=FAKE + 4) == 2
     assert scatter(lib, T=0) == 0  # nothing to do, nothing launched
+
+
+# ---------------------------------------------------------------------------
+# pkv_decode_step: every check of the scatter and of the read runs first
+# ---------------------------------------------------------------------------
+
+def step(lib, d, kn=FAKE, vn=FAKE, sl=FAKE, q=FAKE, wsb=1 << 40):
+    return lib.pkv_decode_step(ctypes.byref(d), kn, vn, sl, q, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(1.0),
+                               FAKE, FAKE, wsb, None)
+
+
+def test_decode_step_refusals(lib):
+    assert step(lib, desc(), kn=0) == 1          # NULL k_new
+    assert step(lib, desc(), sl=FAKE + 4) == 2   # misaligned slot mapping
+    assert step(lib, desc(), q=0) == 1           # the read's own checks
+    assert step(lib, desc(head_dim=96)) == 5
+    assert step(lib, desc(), wsb=16) == 8        # workspace too small
+    assert step(lib, desc(n_kv_heads=5000, n_heads=5000)) in (4, 7)
+
+
+# ---------------------------------------------------------------------------
+# read counters (host arithmetic), pinned to the Day 60 wirebench table
+# ---------------------------------------------------------------------------
+
+from test_oracle_pins import load_wirebench  # noqa: E402
+
+
+@pytest.mark.parametrize("entry", load_wirebench(), ids=lambda e: "rows%d_block%s" % (e["rows"], e["block"]))
+def test_read_counters_reproduce_wirebench(lib, entry):
+    # 2 layers x 47 decode steps, 8 query heads (the page's tiny engine), one
+    # query per row; widths 17..63 for rows 4 and 8, 9..55 for rows 2 (as in
+    # the oracle's pin of the same table)
+    block = entry["block"]
+    c = binding.ReadCounters("gathered" if block is None else "streamed", block or 1)
+    first = 17 if entry["rows"] in (4, 8) else 9
+    for w in range(first, first + 47):
+        for _ in range(2):
+            c.record(entry["rows"], 8, 1, w)
+    assert (c.calls, c.score_cells, c.held_cells) == (entry["reads"], entry["charged"], entry["held"])
+    assert c.rows == entry["rows"] * entry["reads"]
+    assert "%.1fx" % c.saving == entry["saving"]
+
+
+def test_read_counters_window_and_refusals(lib):
+    c = binding.ReadCounters("streamed", 16)
+    assert c.saving == 1.0  # nothing held yet: 1, not "unmeasured"
+    c.record(4, 32, 1, 1000)
+    first = c.snapshot()
+    c.record(4, 32, 1, 1001)
+    w = c.since(first)
+    assert (w.calls, w.rows, w.score_cells, w.held_cells) == (1, 4, 4 * 32 * 1001, 4 * 32 * 16)
+    assert w.saving == pytest.approx(1001 / 16)
+    with pytest.raises(binding.PkvError) as e:  # a reading of another read
+        c.since(binding.ReadCounters("streamed", 32))
+    assert e.value.status == 11
+    with pytest.raises(binding.PkvError) as e:
+        c.since(binding.ReadCounters("gathered", 16))
+    assert e.value.status == 11
+    with pytest.raises(binding.PkvError) as e:  # later minus earlier only
+        first.since(c)
+    assert e.value.status == 7
+    g = binding.ReadCounters("gathered", 1)
+    g.record(3, 8, 2, 40)
+    assert g.held_cells == g.score_cells == 3 * 8 * 2 * 40 and g.saving == 1.0
+    with pytest.raises(binding.PkvError):
+        g.record(-1, 8, 1, 4)
+    with pytest.raises(binding.PkvError):  # 2^31 x 2^31 x 2^31 x 2^31 cells overflow int64
+        g.record(2 ** 31 - 1, 2 ** 31 - 1, 2 ** 31 - 1, 2 ** 31 - 1)
+    assert g.calls == 1
+
+
+def test_read_counters_count_a_descriptor(lib):
+    c = binding.ReadCounters("streamed", 16)
+    d = desc(rows=64, n_heads=32, max_blocks_per_row=256, block_size=16)
+    c.record_read(d)
+    assert (c.calls, c.rows, c.score_cells, c.held_cells) == (1, 64, 64 * 32 * 4096, 64 * 32 * 16)

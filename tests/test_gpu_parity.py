@@ -272,7 +272,7 @@ def test_decode_run_sweep(rows, bs):
     k, v, slots = run.prefill()
     pkv.reshape_and_cache(k, v, slots, run.k_pool, run.v_pool)
     check_oracle = {0, steps // 2, steps - 1}
-    stats = harness.ReadStats("streamed", block=bs)
+    stats = pkv.ReadCounters("streamed", block=bs)
     out = torch.empty(rows, run.n_heads, run.head_dim, dtype=torch.bfloat16, device=DEV)
     for step in range(steps):
         q, kn, vn, sl = run.step()
@@ -294,6 +294,78 @@ def test_decode_run_sweep(rows, bs):
     # run saving: sum of widths over sum of held tiles
     widths = np.arange(513, 513 + steps)
     assert stats.saving == pytest.approx(widths.sum() / np.minimum(bs, widths).sum())
+
+
+# ---------------------------------------------------------------------------
+# one-call decode step, and its replay from a captured HIP graph
+# ---------------------------------------------------------------------------
+
+def test_decode_step_equals_scatter_then_read():
+    run = synth.DecodeRun(rows=32, block_size=16, prompt=200, steps=8, device=DEV, seed=21)
+    k, v, slots = run.prefill()
+    pkv.reshape_and_cache(k, v, slots, run.k_pool, run.v_pool)
+    kp2, vp2 = run.k_pool.clone(), run.v_pool.clone()
+    note("decode step vs scatter + read")
+    for _ in range(run.steps):
+        q, kn, vn, sl = run.step()
+        bt, cl = run.block_table(), run.context_lens()
+        a = pkv.decode_step(q, kn, vn, sl, run.k_pool, run.v_pool, bt, cl, run.scale)
+        pkv.reshape_and_cache(kn, vn, sl, kp2, vp2)
+        b = pkv.paged_attention(q, kp2, vp2, bt, cl, run.scale)
+        torch.cuda.synchronize()
+        assert torch.equal(a, b)
+    assert torch.equal(run.k_pool.view(torch.int16), kp2.view(torch.int16))
+    assert torch.equal(run.v_pool.view(torch.int16), vp2.view(torch.int16))
+
+
+def test_decode_step_replays_from_a_graph():
+    # capture once; every later step copies its inputs into the captured
+    # tensors and replays.  Lengths grow and blocks are allocated between
+    # replays, the launch shape stays rows-only.  Each replay is checked
+    # against the same step run eagerly on a second copy of the pools.
+    rows, bs = 24, 16
+    run = synth.DecodeRun(rows=rows, block_size=bs, prompt=120, steps=24, device=DEV, seed=22)
+    k, v, slots = run.prefill()
+    pkv.reshape_and_cache(k, v, slots, run.k_pool, run.v_pool)
+    kp_ref, vp_ref = run.k_pool.clone(), run.v_pool.clone()
+    q, kn, vn, sl = run.step()
+    bt, cl = run.block_table(), run.context_lens()
+    s_q, s_kn, s_vn, s_sl, s_bt, s_cl = [t.clone() for t in (q, kn, vn, sl, bt, cl)]
+    s_out = torch.empty_like(q)
+    ws = torch.zeros(max(pkv.workspace_size(q, run.k_pool, bt), 1), dtype=torch.uint8, device=DEV)
+    counters = pkv.ReadCounters("streamed", block=bs)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # warm-up outside the capture, on a scratch copy of the pools
+        kw, vw = run.k_pool.clone(), run.v_pool.clone()
+        pkv.decode_step(s_q, s_kn, s_vn, s_sl, kw, vw, s_bt, s_cl, run.scale, out=s_out, workspace=ws)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    del kw, vw
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        pkv.decode_step(s_q, s_kn, s_vn, s_sl, run.k_pool, run.v_pool, s_bt, s_cl, run.scale,
+                        out=s_out, workspace=ws)
+    note("graph replay of decode_step")
+    ref_out = torch.empty_like(q)
+    for i in range(run.steps - 1):
+        if i > 0:
+            q, kn, vn, sl = run.step()
+            bt, cl = run.block_table(), run.context_lens()
+        for dst, src in ((s_q, q), (s_kn, kn), (s_vn, vn), (s_sl, sl), (s_bt, bt), (s_cl, cl)):
+            dst.copy_(src)
+        graph.replay()
+        counters.record(rows, run.n_heads, 1, int(run.ctx_host.max()))
+        pkv.decode_step(q, kn, vn, sl, kp_ref, vp_ref, bt, cl, run.scale, out=ref_out)
+        torch.cuda.synchronize()
+        assert torch.equal(s_out, ref_out), "replay %d" % i
+    assert torch.equal(run.k_pool.view(torch.int16), kp_ref.view(torch.int16))
+    assert torch.equal(run.v_pool.view(torch.int16), vp_ref.view(torch.int16))
+    # and the last replay against the oracle
+    ref = oracle.paged_attention(q.cpu(), run.k_pool.cpu(), run.v_pool.cpu(), run.table_host, run.ctx_host,
+                                 run.scale)
+    assert_close(s_out.float().cpu(), ref, what="graph vs oracle", **TOL[torch.bfloat16])
+    assert counters.calls == run.steps - 1
 
 
 # ---------------------------------------------------------------------------
