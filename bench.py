@@ -189,7 +189,58 @@ def other_workloads(dev, stream):
                               "held_cells": stats.held_cells, "saving": round(stats.saving, 2)}}
             del run, out, steps
     res["decode_run"] = runs
+    res["decode_step_graph"] = graph_step(dev, stream)
     return res
+
+
+def graph_step(dev, stream, reps=100):
+    """The 8B-shaped layer's whole decode step (scatter + read) as one library
+    call, eager and replayed from a captured HIP graph: GPU µs per step (events,
+    host ahead) and wall-clock µs per step for back-to-back steps."""
+    import torch
+
+    import paged_kv_cache_13_amd as pkv
+    from paged_kv_cache_13_amd import synth
+
+    cfg = synth.CONFIGS["llama3_8b_layer"]
+    b = synth.make_batch(cfg, device=dev)
+    bs = cfg.block_size
+    last = b.ctx_host - 1
+    slots = torch.from_numpy((b.table_host[range(cfg.rows), last // bs].astype("int64") * bs + last % bs)).to(dev)
+    g = torch.Generator(device=dev).manual_seed(cfg.seed + 200)
+    kn = torch.randn(cfg.rows, cfg.n_kv_heads, cfg.head_dim, generator=g, device=dev).to(b.q.dtype)
+    vn = torch.randn(cfg.rows, cfg.n_kv_heads, cfg.head_dim, generator=g, device=dev).to(b.q.dtype)
+    out = torch.empty_like(b.q)
+    ws = torch.zeros(max(pkv.workspace_size(b.q, b.k_pool, b.block_table), 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        pkv.decode_step(b.q, kn, vn, slots, b.k_pool, b.v_pool, b.block_table, b.context_lens, b.scale,
+                        out=out, workspace=ws)
+
+    for _ in range(10):
+        step()
+    eager_us, _ = _timed(step, stream, 50)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()
+    torch.cuda.current_stream().wait_stream(side)
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        step()
+    for _ in range(10):
+        graph.replay()
+    graph_us, _ = _timed(graph.replay, stream, 50)
+    walls = {}
+    for name, fn in (("eager", step), ("graph", graph.replay)):
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(reps):
+            fn()
+        torch.cuda.synchronize()
+        walls[name] = (time.perf_counter() - t0) / reps * 1e6
+    return {"workload": cfg.name, "eager_step_us": round(eager_us, 2), "graph_step_us": round(graph_us, 2),
+            "eager_wall_us_per_step": round(walls["eager"], 2), "graph_wall_us_per_step": round(walls["graph"], 2)}
 
 
 def cpu_model():

@@ -14,8 +14,9 @@ Parity pins (tests/test_oracle_pins.py): dense fp64 attention on directly
 built histories, closed forms (one position, zero query, constant V, one
 dominant key), invariants (block permutation, row permutation, slot-mapping vs
 block-table addressing, NaN-poisoned unused slots, GQA vs replicated heads),
-scatter round trip through numpy's view of the layout, and the Day 60 page's
-wirebench cell table.
+scatter round trip through numpy's view of the layout, the Day 60 page's
+wirebench cell table, and for the multi-query read: dense causal attention,
+the one-query case, and each query as a decode read of its own prefix.
 """
 from __future__ import annotations
 
@@ -60,8 +61,11 @@ def _load():
                                                      vp, vp, vp, vp, i64, vp, f64, vp, vp]
         lib.oracle_paged_attention_streamed.argtypes = [i32, i32, i32, i32, i32, i32, i64, i32,
                                                         vp, vp, vp, vp, vp, f64, i32, vp, vp]
+        lib.oracle_paged_attention_multi.argtypes = [i32, i32, i32, i32, i32, i32, i32, i64, i32,
+                                                     vp, vp, vp, vp, vp, f64, vp]
         for fn in (lib.oracle_reshape_and_cache, lib.oracle_paged_attention,
-                   lib.oracle_paged_attention_slots, lib.oracle_paged_attention_streamed):
+                   lib.oracle_paged_attention_slots, lib.oracle_paged_attention_streamed,
+                   lib.oracle_paged_attention_multi):
             fn.restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -160,6 +164,25 @@ def paged_attention(q, k_pool, v_pool, block_table, context_lens, scale):
                                         _ptr(qr), _ptr(kp), _ptr(vp_), _ptr(bt), _ptr(cl),
                                         float(scale), _ptr(out))
     _check(rc, "oracle_paged_attention")
+    return out
+
+
+def paged_attention_multi(q, k_pool, v_pool, block_table, context_lens, scale):
+    """Multi-query read: q [rows, query_len, H, hd] is each row's last
+    query_len positions, causal inside the chunk; returns float64 of q's shape."""
+    if len(q.shape) != 4:
+        raise ValueError("q must be [rows, query_len, n_heads, head_dim]")
+    rows, qlen, n_heads, hd = (int(x) for x in q.shape)
+    qr, kp, vp_, dt, _, _, _, nb, n_kv, bs = _attn_common(q.reshape(rows * qlen, n_heads, hd), k_pool, v_pool)
+    bt = np.ascontiguousarray(np.asarray(block_table, dtype=np.int32))
+    cl = np.ascontiguousarray(np.asarray(context_lens, dtype=np.int32))
+    if bt.ndim != 2 or bt.shape[0] != rows or cl.shape != (rows,):
+        raise ValueError("block_table / context_lens shape mismatch")
+    out = np.zeros((rows, qlen, n_heads, hd), dtype=np.float64)
+    rc = _load().oracle_paged_attention_multi(rows, qlen, n_heads, n_kv, hd, bs, bt.shape[1], nb, dt,
+                                              _ptr(qr), _ptr(kp), _ptr(vp_), _ptr(bt), _ptr(cl),
+                                              float(scale), _ptr(out))
+    _check(rc, "oracle_paged_attention_multi")
     return out
 
 

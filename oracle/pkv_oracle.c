@@ -376,3 +376,85 @@ int oracle_paged_attention_streamed(int32_t rows, int32_t n_heads,
   free(qv); free(st); free(acc);
   return ORC_OK;
 }
+
+/* ------------------------------------------------------------------------ */
+/* Multi-query read (a chunk of query_len new positions per row over the    */
+/* pool, as in chunked prefill): the chunk is the last query_len positions  */
+/* of the row's context, already in the pool.  Query i of row r sits at     */
+/* position p = n - query_len + i and attends causally to t <= p, i.e. to   */
+/* the first p + 1 positions of the assembled history (Day 60 page, "What   */
+/* I added today": the rectangle's query_len axis).  A query with p < 0 has */
+/* no history and reads zeros (the empty-row reading).                      */
+/* q and out are [rows][query_len][n_heads][head_dim].                      */
+/* ------------------------------------------------------------------------ */
+int oracle_paged_attention_multi(int32_t rows, int32_t query_len, int32_t n_heads,
+                                 int32_t n_kv_heads, int32_t head_dim,
+                                 int32_t block_size, int32_t max_blocks_per_row,
+                                 int64_t num_blocks, int32_t dtype, const void *q,
+                                 const void *k_pool, const void *v_pool,
+                                 const int32_t *block_table,
+                                 const int32_t *context_lens, double scale,
+                                 double *out) {
+  int32_t r, i, h, g, d;
+  int32_t group;
+  int64_t t, width;
+  double *Kc, *Vc, *s, *qv;
+  if (!q || !k_pool || !v_pool || !block_table || !context_lens || !out)
+    return ORC_EBADARG;
+  if (rows < 0 || query_len <= 0 || n_heads <= 0 || n_kv_heads <= 0 ||
+      head_dim <= 0 || block_size <= 0 || num_blocks <= 0 ||
+      max_blocks_per_row < 0 || n_heads % n_kv_heads != 0 ||
+      (dtype != ORC_F32 && dtype != ORC_BF16))
+    return ORC_EBADARG;
+  group = n_heads / n_kv_heads;
+  width = (int64_t)max_blocks_per_row * block_size;
+  Kc = (double *)malloc(sizeof(double) * (size_t)(width > 0 ? width : 1) * n_kv_heads * head_dim);
+  Vc = (double *)malloc(sizeof(double) * (size_t)(width > 0 ? width : 1) * n_kv_heads * head_dim);
+  s = (double *)malloc(sizeof(double) * (size_t)(width > 0 ? width : 1));
+  qv = (double *)malloc(sizeof(double) * (size_t)head_dim);
+  if (!Kc || !Vc || !s || !qv) {
+    free(Kc); free(Vc); free(s); free(qv);
+    return ORC_ENOMEM;
+  }
+  for (r = 0; r < rows; ++r) {
+    int64_t n = context_lens[r];
+    if (n < 0 || n > width) {
+      free(Kc); free(Vc); free(s); free(qv);
+      return ORC_ERANGE;
+    }
+    /* The row's history by exact index through its block table. */
+    for (t = 0; t < n; ++t) {
+      int64_t blk = block_table[(size_t)r * max_blocks_per_row + t / block_size];
+      int64_t off = t % block_size;
+      if (blk < 0 || blk >= num_blocks) {
+        free(Kc); free(Vc); free(s); free(qv);
+        return ORC_ERANGE;
+      }
+      for (g = 0; g < n_kv_heads; ++g) {
+        int64_t ksrc = (((int64_t)blk * n_kv_heads + g) * block_size + off) * head_dim;
+        int64_t vtile = ((int64_t)blk * n_kv_heads + g) * head_dim;
+        for (d = 0; d < head_dim; ++d) {
+          Kc[((size_t)t * n_kv_heads + g) * head_dim + d] = widen(k_pool, ksrc + d, dtype);
+          Vc[((size_t)t * n_kv_heads + g) * head_dim + d] =
+              widen(v_pool, (vtile + d) * block_size + off, dtype);
+        }
+      }
+    }
+    for (i = 0; i < query_len; ++i) {
+      int64_t visible = n - query_len + i + 1;  /* positions 0 .. p */
+      for (h = 0; h < n_heads; ++h) {
+        int64_t row = ((int64_t)r * query_len + i) * n_heads + h;
+        if (visible <= 0) {
+          for (d = 0; d < head_dim; ++d) out[row * head_dim + d] = 0.0;
+          continue;
+        }
+        for (d = 0; d < head_dim; ++d) qv[d] = widen(q, row * head_dim + d, dtype);
+        attend_one(qv, Kc + (size_t)(h / group) * head_dim, Vc + (size_t)(h / group) * head_dim,
+                   visible, (int64_t)n_kv_heads * head_dim, head_dim, scale, s,
+                   out + row * head_dim);
+      }
+    }
+  }
+  free(Kc); free(Vc); free(s); free(qv);
+  return ORC_OK;
+}

@@ -416,3 +416,100 @@ def test_fixed_shape_saving_is_width_over_block(w, block):
     _, charged = oracle.paged_attention_slots(q, kp, vp, slots, lens, 1.0)
     _, held = oracle.paged_attention_streamed(q, kp, vp, table, lens, 1.0, block)
     assert Fraction(charged, held) == Fraction(w, block)
+
+
+# ---------------------------------------------------------------------------
+# Multi-query read: a chunk of query_len positions per row, causal inside it
+# ---------------------------------------------------------------------------
+
+def multi_inputs(cfg, qlen, seed=7):
+    b = synth.make_batch(cfg)
+    g = torch.Generator().manual_seed(seed)
+    q = (torch.randn(cfg.rows, qlen, cfg.n_heads, cfg.head_dim, generator=g) * cfg.value_scale).to(b.q.dtype)
+    return b, q
+
+
+def causal_sdpa_reference(b, q):
+    """torch fp64 SDPA with an explicit mask: query i of row r (position
+    n - qlen + i) sees history positions t <= n - qlen + i."""
+    cfg = b.cfg
+    G = cfg.n_heads // cfg.n_kv_heads
+    rows, qlen = q.shape[0], q.shape[1]
+    kp = b.k_pool.to(torch.float64).numpy()
+    vp = b.v_pool.to(torch.float64).numpy()
+    out = np.zeros((rows, qlen, cfg.n_heads, cfg.head_dim))
+    for r in range(rows):
+        n = int(b.ctx_host[r])
+        if n == 0:
+            continue
+        K = torch.from_numpy(assembled_history(kp, b.table_host[r], n, cfg.block_size))
+        V = torch.from_numpy(assembled_history_v(vp, b.table_host[r], n, cfg.block_size))
+        K = K.permute(1, 0, 2).repeat_interleave(G, dim=0).contiguous()  # [H, n, hd]
+        V = V.permute(1, 0, 2).repeat_interleave(G, dim=0).contiguous()
+        pos = torch.arange(n)[None, :]
+        qpos = (n - qlen + torch.arange(qlen))[:, None]
+        mask = pos <= qpos                                                  # [qlen, n]
+        qq = q[r].to(torch.float64).permute(1, 0, 2).contiguous()           # [H, qlen, hd]
+        o = torch.nn.functional.scaled_dot_product_attention(qq, K, V, attn_mask=mask, scale=cfg.scale)
+        o = o.permute(1, 0, 2).numpy()                                      # [qlen, H, hd]
+        seen = (qpos[:, 0] >= 0).numpy()
+        out[r][seen] = o[seen]
+    return out
+
+
+MULTI_CASES = [
+    (small_cfg("f32_q3", "f32", rows=3, H=8, KV=2, hd=16, bs=8, lo=1, hi=60, seed=31), 3),
+    (small_cfg("bf16_q7", "bf16", rows=3, H=8, KV=2, hd=64, bs=16, lo=1, hi=60, seed=32), 7),
+    (small_cfg("f32_q16_mha", "f32", rows=2, H=4, KV=4, hd=16, bs=32, lo=10, hi=90, seed=33), 16),
+    (small_cfg("bf16_q5_g8", "bf16", rows=4, H=8, KV=1, hd=16, bs=8, lo=1, hi=30, seed=34), 5),
+]
+
+
+@pytest.mark.parametrize("cfg,qlen", MULTI_CASES, ids=lambda c: getattr(c, "name", str(c)))
+def test_multi_query_oracle_matches_causal_sdpa(cfg, qlen):
+    b, q = multi_inputs(cfg, qlen)
+    got = oracle.paged_attention_multi(q, b.k_pool, b.v_pool, b.table_host, b.ctx_host, b.scale)
+    assert np.isfinite(got).all()
+    np.testing.assert_allclose(got, causal_sdpa_reference(b, q), **F64_TOL)
+
+
+@pytest.mark.parametrize("cfg,qlen", MULTI_CASES[:2], ids=lambda c: getattr(c, "name", str(c)))
+def test_multi_query_is_a_decode_read_of_each_prefix(cfg, qlen):
+    # query i of a row of length n reads exactly what a one-query read of the
+    # same row truncated to n - qlen + i + 1 positions reads
+    b, q = multi_inputs(cfg, qlen)
+    got = oracle.paged_attention_multi(q, b.k_pool, b.v_pool, b.table_host, b.ctx_host, b.scale)
+    for i in range(qlen):
+        lens = np.maximum(b.ctx_host - qlen + i + 1, 0).astype(np.int32)
+        ref = oracle.paged_attention(q[:, i].contiguous(), b.k_pool, b.v_pool, b.table_host, lens, b.scale)
+        np.testing.assert_array_equal(got[:, i], ref)
+
+
+def test_multi_query_of_one_is_the_decode_read():
+    cfg = CASES[1]
+    b = synth.make_batch(cfg)
+    got = oracle.paged_attention_multi(b.q[:, None].contiguous(), b.k_pool, b.v_pool, b.table_host,
+                                       b.ctx_host, b.scale)
+    np.testing.assert_array_equal(got[:, 0], run_oracle(b))
+
+
+def test_multi_query_before_the_history_reads_zeros():
+    # rows shorter than the chunk: the queries at negative positions see nothing
+    cfg = small_cfg("short", "f32", rows=2, H=4, KV=2, hd=16, bs=8, lo=2, hi=4, seed=35)
+    b, q = multi_inputs(cfg, 6)
+    got = oracle.paged_attention_multi(q, b.k_pool, b.v_pool, b.table_host, b.ctx_host, b.scale)
+    for r in range(cfg.rows):
+        n = int(b.ctx_host[r])
+        assert (got[r, :6 - n] == 0).all()
+        assert (np.abs(got[r, 6 - n:]).sum(axis=-1) > 0).all()
+
+
+def test_multi_query_block_permutation_is_bitwise_invariant():
+    cfg, qlen = MULTI_CASES[1]
+    b, q = multi_inputs(cfg, qlen)
+    base = oracle.paged_attention_multi(q, b.k_pool, b.v_pool, b.table_host, b.ctx_host, b.scale)
+    perm = np.random.default_rng(5).permutation(b.num_blocks)
+    inv = torch.as_tensor(np.argsort(perm))
+    got = oracle.paged_attention_multi(q, b.k_pool[inv], b.v_pool[inv], perm[b.table_host].astype(np.int32),
+                                       b.ctx_host, b.scale)
+    np.testing.assert_array_equal(base, got)
