@@ -159,6 +159,35 @@ int pkv_paged_attention(const pkv_attn_desc *d, const void *q, const void *k_poo
 size_t pkv_paged_attention_workspace_size(const pkv_attn_desc *d);
 
 /*
+ * pkv_paged_attention_multi -- the paged read for a chunk of query_len
+ * queries per row (chunked prefill over the pool): the rectangle's query_len
+ * axis of the "Day 60" page, "What I added today", with a causal mask inside
+ * the chunk.
+ *
+ * The chunk is each row's last query_len positions, already scattered into
+ * the pool and counted in context_lens[r] = n.  Query i (0 <= i < query_len)
+ * sits at position p = n - query_len + i and attends to positions 0 .. p:
+ *   s_t = scale * <q[r,i,h,:], K_t>,  out[r,i,h,:] = sum_{t<=p} softmax(s)_t V_t.
+ * A query with p < 0 (a row shorter than the chunk) reads zeros.  With
+ * query_len = 1 this is pkv_paged_attention.
+ *
+ *   d             as for pkv_paged_attention; dtype must be PKV_BF16 and
+ *                 head_dim 64 or 128 (else PKV_ERR_DTYPE / PKV_ERR_HEAD_DIM);
+ *                 partition_tokens is rounded up to a multiple of 32
+ *   query_len     1 .. 65535
+ *   q, out        device [rows, query_len, n_heads, head_dim]
+ *   workspace     >= pkv_paged_attention_multi_workspace_size(d, query_len)
+ *                 bytes (NULL allowed when that is 0)
+ */
+int pkv_paged_attention_multi(const pkv_attn_desc *d, int32_t query_len, const void *q,
+                              const void *k_pool, const void *v_pool, const int32_t *block_table,
+                              const int32_t *context_lens, float scale, void *out, void *workspace,
+                              size_t workspace_bytes, void *stream);
+
+/* Workspace bytes of pkv_paged_attention_multi (0 for an invalid request). */
+size_t pkv_paged_attention_multi_workspace_size(const pkv_attn_desc *d, int32_t query_len);
+
+/*
  * pkv_decode_step -- one decode step of every row: append the step's new
  * token, then read.  ("Day 60" page, "Tomorrow": with the streamed read a
  * decode step presents a shape of rows and nothing else.)

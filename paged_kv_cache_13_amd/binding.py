@@ -73,6 +73,11 @@ def load_library():
     lib.pkv_strerror.restype = ctypes.c_char_p
     lib.pkv_version.argtypes = []
     lib.pkv_version.restype = ctypes.c_int
+    lib.pkv_paged_attention_multi.argtypes = [ctypes.POINTER(AttnDesc), i32, vp, vp, vp, vp, vp,
+                                              ctypes.c_float, vp, vp, sz, vp]
+    lib.pkv_paged_attention_multi.restype = ctypes.c_int
+    lib.pkv_paged_attention_multi_workspace_size.argtypes = [ctypes.POINTER(AttnDesc), i32]
+    lib.pkv_paged_attention_multi_workspace_size.restype = sz
     lib.pkv_decode_step.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp,
                                     ctypes.c_float, vp, vp, sz, vp]
     lib.pkv_decode_step.restype = ctypes.c_int
@@ -202,6 +207,45 @@ def paged_attention_into(q, k_pool, v_pool, block_table, context_lens, scale, ou
         wsp, wsb, _stream_handle(dev)))
     if stats is not None:
         stats.record_read(d)
+    return out
+
+
+def paged_attention_multi(q, k_pool, v_pool, block_table, context_lens, scale, out=None,
+                          workspace: Optional[torch.Tensor] = None, partition_tokens: int = 0,
+                          stats: Optional["ReadCounters"] = None) -> torch.Tensor:
+    """Paged read of a chunk of queries per row: q [rows, query_len, n_heads,
+    hd] holds each row's last query_len positions (already in the pool and
+    counted in context_lens), causal inside the chunk.  Returns (or writes
+    into `out`) [rows, query_len, n_heads, hd]."""
+    if out is None:
+        out = torch.empty_like(q)
+    dev = _on_gpu(q, k_pool, v_pool, block_table, context_lens, out)
+    _require(q.dim() == 4, "q must be [rows, query_len, n_heads, head_dim]")
+    _check_pools(k_pool, v_pool)
+    _require(k_pool.dtype == q.dtype and v_pool.dtype == q.dtype, "q and pools must share one dtype")
+    _require(block_table.dtype == torch.int32 and block_table.dim() == 2
+             and block_table.shape[0] == q.shape[0], "block_table must be int32 [rows, max_blocks]")
+    _require(context_lens.dtype == torch.int32 and context_lens.shape == (q.shape[0],),
+             "context_lens must be int32 [rows]")
+    _require(out.shape == q.shape, "out must be q's shape")
+    rows, qlen, n_heads, hd = q.shape
+    nb, nkv, bs, hd2 = k_pool.shape
+    _require(hd == hd2, "q and pools disagree on head_dim")
+    d = AttnDesc(rows=rows, n_heads=n_heads, n_kv_heads=nkv, head_dim=hd, block_size=bs,
+                 max_blocks_per_row=block_table.shape[1], num_blocks=nb, dtype=_dtype_code(q),
+                 out_dtype=_dtype_code(out), partition_tokens=int(partition_tokens))
+    lib = load_library()
+    need = int(lib.pkv_paged_attention_multi_workspace_size(ctypes.byref(d), qlen))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+    else:
+        _on_gpu(workspace)
+    _check(lib.pkv_paged_attention_multi(
+        ctypes.byref(d), qlen, q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), block_table.data_ptr(),
+        context_lens.data_ptr(), ctypes.c_float(scale), out.data_ptr(), workspace.data_ptr() if need else None,
+        workspace.numel() * workspace.element_size(), _stream_handle(dev)))
+    if stats is not None:
+        stats.record(rows, n_heads, qlen, block_table.shape[1] * bs)
     return out
 
 

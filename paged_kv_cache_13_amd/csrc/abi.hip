@@ -106,6 +106,48 @@ int plan_decode(const pkv_attn_desc *d, Plan *pl) {
   return PKV_OK;
 }
 
+// Multi-query read: bf16, head_dim 64/128.  Partitions are whole 32-position
+// groups: the caller's partition_tokens rounded up to one, else a default
+// that fills about kTargetMultiUnits waves.
+constexpr int64_t kTargetMultiUnits = 1024;
+struct MultiPlan {
+  int32_t q_tiles, q_per_tile;
+};
+int plan_multi(const pkv_attn_desc *d, int32_t query_len, Plan *pl, MultiPlan *mp) {
+  const int st = plan_decode(d, pl);
+  if (st != PKV_OK) return st;
+  if (d->dtype != PKV_BF16) return PKV_ERR_DTYPE;
+  if (d->head_dim != 64 && d->head_dim != 128) return PKV_ERR_HEAD_DIM;
+  if (query_len < 1 || query_len > 65535) return PKV_ERR_SHAPE;
+  const int32_t cap = d->max_blocks_per_row * d->block_size;
+  mp->q_per_tile = 16 / pl->group;
+  mp->q_tiles = (query_len + mp->q_per_tile - 1) / mp->q_per_tile;
+  const int64_t g32 = pkv::kGroupPositions;
+  int64_t part;
+  if (d->partition_tokens) {
+    part = (d->partition_tokens + g32 - 1) / g32 * g32;
+  } else {
+    const int64_t tiles = (int64_t)mp->q_tiles * d->n_kv_heads * (d->rows > 0 ? d->rows : 1);
+    const int64_t want = (kTargetMultiUnits + tiles - 1) / tiles;
+    part = ((cap + want - 1) / want + g32 - 1) / g32 * g32;
+    if (part > kDefaultPartition) part = kDefaultPartition;
+  }
+  if (part < g32) part = g32;
+  const int64_t cap32 = (cap + g32 - 1) / g32 * g32;
+  if (part > cap32) part = cap32;
+  pl->partition = (int32_t)part;
+  pl->max_parts = (int32_t)((cap + part - 1) / part);
+  const int64_t units = (int64_t)pl->max_parts * mp->q_tiles * d->n_kv_heads * d->rows;
+  const int64_t vrows = (int64_t)d->rows * query_len;
+  if (units > INT_MAX || vrows * d->n_heads > INT_MAX) return PKV_ERR_SHAPE;
+  pl->stream = 0;
+  pl->ws_bytes = 0;
+  if (pl->max_parts > 1 && d->rows > 0)
+    pl->ws_bytes =
+        pkv::ws_layout((int32_t)vrows, d->n_heads, pl->max_parts, d->head_dim).total_floats * sizeof(float);
+  return PKV_OK;
+}
+
 int check_scatter(const void *k, const void *v, const int64_t *slot_mapping, int64_t num_tokens,
                   const void *k_pool, const void *v_pool, int64_t num_blocks, int32_t block_size,
                   int32_t n_kv_heads, int32_t head_dim, int32_t dtype);
@@ -237,6 +279,57 @@ int pkv_paged_attention(const pkv_attn_desc *d, const void *q, const void *k_poo
   if (st != PKV_OK) return st;
   return launch_attention(d, pl, q, k_pool, v_pool, block_table, context_lens, scale, out, workspace,
                           static_cast<hipStream_t>(stream));
+}
+
+size_t pkv_paged_attention_multi_workspace_size(const pkv_attn_desc *d, int32_t query_len) {
+  Plan pl;
+  MultiPlan mp;
+  if (plan_multi(d, query_len, &pl, &mp) != PKV_OK) return 0;
+  return pl.ws_bytes;
+}
+
+int pkv_paged_attention_multi(const pkv_attn_desc *d, int32_t query_len, const void *q, const void *k_pool,
+                              const void *v_pool, const int32_t *block_table, const int32_t *context_lens,
+                              float scale, void *out, void *workspace, size_t workspace_bytes, void *stream) {
+  Plan pl;
+  MultiPlan mp;
+  const int st = plan_multi(d, query_len, &pl, &mp);
+  if (st != PKV_OK) return st;
+  if (!q || !k_pool || !v_pool || !block_table || !context_lens || !out) return PKV_ERR_NULL;
+  if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16) ||
+      !aligned(block_table, 4) || !aligned(context_lens, 4))
+    return PKV_ERR_ALIGN;
+  if (pl.ws_bytes > 0) {
+    if (!workspace || workspace_bytes < pl.ws_bytes) return PKV_ERR_WORKSPACE;
+    if (!aligned(workspace, 16)) return PKV_ERR_ALIGN;
+  }
+  if (d->rows == 0) return PKV_OK;
+  pkv::DecodeArgs a = {};
+  a.q = q;
+  a.k_pool = k_pool;
+  a.v_pool = v_pool;
+  a.block_table = block_table;
+  a.context_lens = context_lens;
+  a.out = out;
+  a.ws = pl.ws_bytes ? static_cast<float *>(workspace) : nullptr;
+  a.rows = d->rows;
+  a.n_heads = d->n_heads;
+  a.n_kv_heads = d->n_kv_heads;
+  a.group = pl.group;
+  a.head_dim = d->head_dim;
+  a.block_size = d->block_size;
+  a.log2_bs = pl.log2_bs;
+  a.max_blocks_per_row = d->max_blocks_per_row;
+  a.partition_tokens = pl.partition;
+  a.max_parts = pl.max_parts;
+  a.num_blocks = d->num_blocks;
+  a.dtype = d->dtype;
+  a.out_dtype = d->out_dtype;
+  a.scale = scale;
+  a.query_len = query_len;
+  a.q_tiles = mp.q_tiles;
+  a.q_per_tile = mp.q_per_tile;
+  return pkv::launch_multi(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
 int pkv_decode_step(const pkv_attn_desc *d, const void *k_new, const void *v_new,

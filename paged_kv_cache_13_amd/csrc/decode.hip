@@ -1352,6 +1352,211 @@ hipError_t launch_dt(const DecodeArgs &a, hipStream_t s) {
   }
 }
 
+// ---------------------------------------------------------------------------
+// Multi-query read: each row brings a chunk of query_len queries, its last
+// query_len positions (already in the pool), causal inside the chunk -- query
+// i at position n - query_len + i sees positions 0 .. n - query_len + i.
+//
+// The 16 columns of the score tile S^T = K Q^T hold (query, head) pairs:
+// 16 / group queries of one kv head's group per tile.  One wave per
+// (position partition, query tile, kv head, row) walks its partition's
+// 32-position groups -- only those some query of the tile can see -- with the
+// same LDS-staged K/V and MFMA tiles as the one-query read, a per-column
+// causal bound on the scores, and an online softmax that tolerates a column
+// with nothing visible yet.  Rows of one partition are written directly;
+// longer rows leave per-partition (max, sum, acc) for decode_multi_merge.
+// ---------------------------------------------------------------------------
+template <int HD>
+__device__ __forceinline__ void group_softmax_pv_causal(const f32x4_t (&sacc)[2], bf16x8_t (&v)[HD / 16],
+                                                        f32x4_t *acc, float &m, float &l, float c, int col_end,
+                                                        int row_end, int gbase, int lg) {
+  constexpr int DT = HD / 16;
+  const int tl = gbase + 8 * lg;
+  float s[8];
+#pragma unroll
+  for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) s[4 * tt + j] = (tl + 4 * tt + j < col_end) ? sacc[tt][j] * c : -INFINITY;
+  float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
+  mx = max_across_rows(mx);
+  const float m_new = fmaxf(m, mx);
+  const float alpha = (m == m_new) ? 1.f : exp2_fast(m - m_new);
+  m = m_new;
+  float pv[8], psum = 0.f;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    pv[e] = s[e] == -INFINITY ? 0.f : exp2_fast(s[e] - m_new);  // nothing visible yet: m_new is -inf too
+    psum += pv[e];
+  }
+  l = l * alpha + psum;
+  if (__any(alpha != 1.f)) {
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
+  }
+  uint32_t hw[4], lw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t h0 = bf16_bits_rne(pv[2 * i]), h1 = bf16_bits_rne(pv[2 * i + 1]);
+    const float r0 = pv[2 * i] - __builtin_bit_cast(float, h0 << 16);
+    const float r1 = pv[2 * i + 1] - __builtin_bit_cast(float, h1 << 16);
+    hw[i] = h0 | (h1 << 16);
+    lw[i] = bf16_bits_rne(r0) | (bf16_bits_rne(r1) << 16);
+  }
+  const bf16x8_t phi = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+  const bf16x8_t plo = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+  if (gbase + 32 > row_end) {  // positions past the row end: zero their (possibly NaN) V
+    int nv = row_end - tl;
+    nv = nv < 0 ? 0 : (nv > 8 ? 8 : nv);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) v[dt] = keep_first(v[dt], nv);
+  }
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) {
+    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v[dt], phi, acc[dt], 0, 0, 0);
+    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v[dt], plo, acc[dt], 0, 0, 0);
+  }
+}
+
+template <int HD, int BS>
+__global__ __launch_bounds__(kWave) void decode_multi(DecodeArgs a) {
+  constexpr int KS = HD / 32, DT = HD / 16;
+  __shared__ uint4 s_k[2 * KS * kWave];
+  __shared__ uint4 s_v[DT * kWave];
+  const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
+  const int G = a.group, Q = a.query_len, QB = a.q_per_tile, P = a.partition_tokens;
+  long long u = blockIdx.x;  // kv head fastest (spread over XCDs), then row, query tile, partition
+  const int kvh = (int)(u % a.n_kv_heads);
+  u /= a.n_kv_heads;
+  const int r = (int)(u % a.rows);
+  u /= a.rows;
+  const int qt = (int)(u % a.q_tiles);
+  const int part = (int)(u / a.q_tiles);
+  const int cap = a.max_blocks_per_row * a.block_size;
+  int n = a.context_lens[r];
+  n = n < 0 ? 0 : (n > cap ? cap : n);
+  const int nparts = n > 0 ? (n + P - 1) / P : 1;
+  if (part >= nparts) return;
+  // this lane's column: query qi, head kvh * G + hi
+  const int qi = qt * QB + lr / G, hi = lr % G;
+  const bool col = lr < QB * G && qi < Q;
+  const int col_end = col ? max(n - Q + qi + 1, 0) : 0;  // positions this query sees
+  const int q_last = min(Q - 1, qt * QB + QB - 1);
+  const int pos0 = part * P;
+  const int unit_end = max(min(pos0 + P, n - Q + q_last + 1), pos0);  // some query sees positions below
+  bf16x8_t qb[KS];
+#pragma unroll
+  for (int i = 0; i < KS; ++i)
+    qb[i] = col ? ld_bf16x8(a.q, ((((size_t)r * Q + qi) * a.n_heads + kvh * G + hi) * HD + (4 * i + lg) * 8) * 2)
+                : zero_bf16x8();
+  const float cscale = a.scale * kLog2e;
+  float m = -INFINITY, l = 0.f;
+  f32x4_t acc[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+
+  const int g0 = pos0 / kGroupPositions, g1 = (unit_end + kGroupPositions - 1) / kGroupPositions;
+  Cursor c;
+  c.kvh = kvh;
+  c.r = r;
+  c.n = n;
+  GroupIds ids1;
+  if (g0 < g1) {
+    c.j = g0;
+    const GroupIds ids0 = load_ids<BS>(a, c, lr, lg);
+    stage_group<HD, BS>(s_k, s_v, a, c, ids0, lane, lr, lg);
+    if (g0 + 1 < g1) {
+      c.j = g0 + 1;
+      ids1 = load_ids<BS>(a, c, lr, lg);
+    }
+  }
+  bf16x8_t kc[2][KS], vc[DT];
+  for (int g = g0; g < g1; ++g) {
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the staged group has landed (LDS DMA is not ordered for us)
+    asm volatile("" ::: "memory");
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt)
+#pragma unroll
+      for (int i = 0; i < KS; ++i) kc[tt][i] = __builtin_bit_cast(bf16x8_t, s_k[(tt * KS + i) * kWave + lane]);
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vc[dt] = __builtin_bit_cast(bf16x8_t, s_v[dt * kWave + lane]);
+    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the buffer may be refilled
+    asm volatile("" ::: "memory");
+    if (g + 1 < g1) {
+      c.j = g + 1;
+      stage_group<HD, BS>(s_k, s_v, a, c, ids1, lane, lr, lg);
+      if (g + 2 < g1) {
+        c.j = g + 2;
+        ids1 = load_ids<BS>(a, c, lr, lg);
+      }
+    }
+    f32x4_t sacc[2];
+    group_scores<HD>(kc, qb, sacc);
+    group_softmax_pv_causal<HD>(sacc, vc, acc, m, l, cscale, col_end, n, g * kGroupPositions, lg);
+  }
+  const float lt = sum_across_rows(l);
+  if (!col) return;
+  const size_t vrow_head = ((size_t)r * Q + qi) * a.n_heads + kvh * G + hi;
+  if (nparts == 1) {
+    const float inv = lt > 0.f ? 1.f / lt : 0.f;  // a query before the history reads zeros
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) store_out(a.out, a.out_dtype, vrow_head * HD + 16 * dt + 4 * lg + e, acc[dt][e] * inv);
+  } else {
+    const WsLayout W = ws_layout(a.rows * Q, a.n_heads, a.max_parts, HD);
+    const size_t slot = vrow_head * a.max_parts + part;
+    float *accp = a.ws + W.acc_off + slot * HD;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4_t *>(accp + 16 * dt + 4 * lg) = acc[dt];
+    if (lg == 0) {
+      a.ws[W.m_off + slot] = m;
+      a.ws[W.l_off + slot] = lt;
+    }
+  }
+}
+
+// Combine the partitions of one (row, query, head) of the multi-query read:
+// M = max_k m_k over partitions that saw something; out = sum_k acc_k 2^(m_k - M)
+// / sum_k l_k 2^(m_k - M), or zeros when no partition saw a position.
+__global__ __launch_bounds__(128) void decode_multi_merge(DecodeArgs a) {
+  const int Q = a.query_len, HD = a.head_dim;
+  const size_t vh = blockIdx.x;  // ((row * Q + query) * n_heads + head)
+  const int r = (int)(vh / ((size_t)Q * a.n_heads));
+  const int cap = a.max_blocks_per_row * a.block_size;
+  int n = a.context_lens[r];
+  n = n < 0 ? 0 : (n > cap ? cap : n);
+  const int nparts = n > 0 ? (n + a.partition_tokens - 1) / a.partition_tokens : 1;
+  if (nparts <= 1) return;
+  const WsLayout W = ws_layout(a.rows * Q, a.n_heads, a.max_parts, HD);
+  const size_t s0 = vh * a.max_parts;
+  float M = -INFINITY;
+  for (int k = 0; k < nparts; ++k) M = fmaxf(M, a.ws[W.m_off + s0 + k]);
+  for (int d = threadIdx.x; d < HD; d += blockDim.x) {
+    float L = 0.f, O = 0.f;
+    if (M != -INFINITY) {
+      for (int k = 0; k < nparts; ++k) {
+        const float mk = a.ws[W.m_off + s0 + k];
+        if (mk == -INFINITY) continue;
+        const float w = exp2_fast(mk - M);
+        L = fmaf(a.ws[W.l_off + s0 + k], w, L);
+        O = fmaf(a.ws[W.acc_off + (s0 + k) * HD + d], w, O);
+      }
+    }
+    store_out(a.out, a.out_dtype, vh * HD + d, L > 0.f ? O / L : 0.f);
+  }
+}
+
+template <int HD, int BS>
+hipError_t launch_multi_t(const DecodeArgs &a, hipStream_t stream) {
+  const long long units = (long long)a.max_parts * a.q_tiles * a.rows * a.n_kv_heads;
+  hipLaunchKernelGGL((decode_multi<HD, BS>), dim3((unsigned)units), dim3(kWave), 0, stream, a);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || a.max_parts <= 1) return e;
+  hipLaunchKernelGGL(decode_multi_merge, dim3((unsigned)((size_t)a.rows * a.query_len * a.n_heads)), dim3(128), 0,
+                     stream, a);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
@@ -1377,6 +1582,17 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
     return launch_mfma<64, 32>(a, stream);
   }
   return launch_dt<uint16_t>(a, stream);
+}
+
+hipError_t launch_multi(const DecodeArgs &a, hipStream_t stream) {
+  if (a.head_dim == 128) {
+    if (a.block_size == 8) return launch_multi_t<128, 8>(a, stream);
+    if (a.block_size == 16) return launch_multi_t<128, 16>(a, stream);
+    return launch_multi_t<128, 32>(a, stream);
+  }
+  if (a.block_size == 8) return launch_multi_t<64, 8>(a, stream);
+  if (a.block_size == 16) return launch_multi_t<64, 16>(a, stream);
+  return launch_multi_t<64, 32>(a, stream);
 }
 
 }  // namespace pkv

@@ -25,6 +25,8 @@ struct DecodeArgs {
   int64_t num_blocks;
   int32_t dtype, out_dtype;
   float scale;
+  // multi-query read: queries per row, query tiles per row, queries per tile
+  int32_t query_len, q_tiles, q_per_tile;
 };
 
 // Workspace of the split-context read, in floats: running max m and sum l
@@ -74,6 +76,7 @@ __host__ __device__ inline StreamLayout stream_layout(int32_t rows, int32_t n_kv
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);
+hipError_t launch_multi(const DecodeArgs &a, hipStream_t stream);
 
 hipError_t launch_scatter(const void *k, const void *v, const int64_t *slots, int64_t num_tokens,
                           void *k_pool, void *v_pool, int64_t num_blocks, int32_t block_size,

@@ -31,6 +31,7 @@ def declared_functions():
 
 def test_header_declares_the_entry_points():
     assert declared_functions() == ["pkv_decode_step", "pkv_paged_attention",
+                                    "pkv_paged_attention_multi", "pkv_paged_attention_multi_workspace_size",
                                     "pkv_paged_attention_workspace_size", "pkv_read_stats_init",
                                     "pkv_read_stats_record", "pkv_read_stats_record_read",
                                     "pkv_read_stats_saving", "pkv_read_stats_since",
@@ -223,3 +224,33 @@ def test_read_counters_count_a_descriptor(lib):
     d = desc(rows=64, n_heads=32, max_blocks_per_row=256, block_size=16)
     c.record_read(d)
     assert (c.calls, c.rows, c.score_cells, c.held_cells) == (1, 64, 64 * 32 * 4096, 64 * 32 * 16)
+
+
+# ---------------------------------------------------------------------------
+# multi-query read: host-side plan and refusals
+# ---------------------------------------------------------------------------
+
+def multi(lib, d, qlen, q=FAKE, wsb=1 << 40):
+    return lib.pkv_paged_attention_multi(ctypes.byref(d), qlen, q, FAKE, FAKE, FAKE, FAKE, ctypes.c_float(1.0),
+                                         FAKE, FAKE, wsb, None)
+
+
+def test_multi_query_refusals(lib):
+    assert multi(lib, desc(dtype=0, out_dtype=0), 4) == 3     # fp32: not supported by this read
+    assert multi(lib, desc(head_dim=16), 4) == 5
+    assert multi(lib, desc(), 0) == 7
+    assert multi(lib, desc(), 70000) == 7
+    assert multi(lib, desc(), 4, q=0) == 1
+    assert multi(lib, desc(), 4, wsb=8) == 8
+
+
+def test_multi_query_workspace(lib):
+    ws = lambda d, q: lib.pkv_paged_attention_multi_workspace_size(ctypes.byref(d), q)
+    # 64 rows x 8 kv heads x one 4-query tile = 512 tiles: two waves per tile
+    # wanted gives 2048 positions, capped at 512, so a 4096-position table
+    # splits in 8: m, l and a 128-float acc per (row, query, head, partition)
+    d = desc()
+    slots = 64 * 4 * 32 * 8
+    assert ws(d, 4) == (((2 * slots + 3) & ~3) + slots * 128) * 4
+    assert ws(desc(partition_tokens=4096), 4) == 0   # one partition: written directly
+    assert ws(desc(dtype=0, out_dtype=0), 4) == 0    # refused descriptors need nothing

@@ -430,3 +430,78 @@ def test_read_many_rows(rows):
     got = gpu_read(b, out_dtype=torch.float32)[torch.as_tensor(sample, device=DEV)].cpu().numpy()
     assert_close(got, ref, what="rows=%d" % rows, **TOL[torch.float32])
     assert (b.ctx_host == 0).any()
+
+
+# ---------------------------------------------------------------------------
+# multi-query read (a chunk of queries per row, causal inside the chunk)
+# ---------------------------------------------------------------------------
+
+def multi_case(rows, H, KV, hd, bs, lo, hi, qlen, seed, value_scale=1.0):
+    cfg = synth.DecodeConfig("multi", "bf16", rows=rows, n_heads=H, n_kv_heads=KV, head_dim=hd, block_size=bs,
+                             ctx=("uniform", lo, hi), pool=("factor", 1.5), max_ctx=max(hi, bs),
+                             value_scale=value_scale, seed=seed)
+    b = synth.make_batch(cfg, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(seed + 1)
+    q = (torch.randn(rows, qlen, H, hd, generator=g, device=DEV) * value_scale).to(torch.bfloat16)
+    return b, q
+
+
+def multi_oracle(b, q):
+    return oracle.paged_attention_multi(q.cpu(), b.k_pool.cpu(), b.v_pool.cpu(), b.table_host, b.ctx_host, b.scale)
+
+
+@pytest.mark.parametrize("H,KV,hd,bs,lo,hi,qlen,part", [
+    (32, 8, 128, 16, 1, 300, 1, 0), (32, 8, 128, 16, 1, 300, 4, 0), (32, 8, 128, 16, 1, 300, 5, 0),
+    (32, 8, 128, 16, 40, 300, 16, 0), (32, 8, 128, 8, 60, 400, 33, 64), (32, 8, 128, 32, 1, 400, 8, 32),
+    (8, 1, 64, 16, 1, 200, 6, 0), (8, 1, 64, 8, 100, 500, 3, 96), (16, 16, 64, 32, 1, 150, 2, 0),
+    (24, 2, 128, 16, 1, 260, 7, 64),
+])
+def test_multi_query_read_matches_oracle(H, KV, hd, bs, lo, hi, qlen, part):
+    note("multi H=%d KV=%d hd=%d bs=%d q=%d part=%d" % (H, KV, hd, bs, qlen, part))
+    b, q = multi_case(5, H, KV, hd, bs, lo, hi, qlen, seed=hd + bs + qlen)
+    got = pkv.paged_attention_multi(q, b.k_pool, b.v_pool, b.block_table, b.context_lens, b.scale,
+                                    partition_tokens=part)
+    got32 = pkv.paged_attention_multi(q, b.k_pool, b.v_pool, b.block_table, b.context_lens, b.scale,
+                                      out=torch.empty(q.shape, dtype=torch.float32, device=DEV),
+                                      partition_tokens=part)
+    torch.cuda.synchronize()
+    ref = multi_oracle(b, q)
+    assert_close(got.float().cpu(), ref, what="multi bf16 out", **TOL[torch.bfloat16])
+    assert_close(got32.cpu(), ref, what="multi fp32 out", **TOL[torch.float32])
+
+
+def test_multi_query_rows_shorter_than_the_chunk_read_zeros():
+    b, q = multi_case(6, 32, 8, 128, 16, 1, 6, 8, seed=41)
+    got = pkv.paged_attention_multi(q, b.k_pool, b.v_pool, b.block_table, b.context_lens, b.scale)
+    torch.cuda.synchronize()
+    ref = multi_oracle(b, q)
+    assert_close(got.float().cpu(), ref, what="short rows", **TOL[torch.bfloat16])
+    for r in range(6):
+        n = int(b.ctx_host[r])
+        assert (got[r, :8 - n].float() == 0).all()
+
+
+def test_multi_query_of_one_matches_the_decode_read():
+    b, q = multi_case(16, 32, 8, 128, 16, 1, 2000, 1, seed=42)
+    multi = pkv.paged_attention_multi(q, b.k_pool, b.v_pool, b.block_table, b.context_lens, b.scale,
+                                      out=torch.empty(q.shape, dtype=torch.float32, device=DEV))
+    dec = pkv.paged_attention(q[:, 0].contiguous(), b.k_pool, b.v_pool, b.block_table, b.context_lens,
+                              b.scale, out=torch.empty(q[:, 0].shape, dtype=torch.float32, device=DEV))
+    torch.cuda.synchronize()
+    assert_close(multi[:, 0].cpu(), dec.cpu(), what="q=1 vs decode", atol=2e-6, rtol=1e-5)
+
+
+def test_multi_query_prefill_chunk_sampled():
+    # Llama-3-8B-shaped chunked prefill: 64-query chunks at the end of rows
+    # up to 3000 positions; a sample of (row, query) pairs checked one by one
+    b, q = multi_case(3, 32, 8, 128, 16, 1500, 3000, 64, seed=43)
+    got = pkv.paged_attention_multi(q, b.k_pool, b.v_pool, b.block_table, b.context_lens, b.scale,
+                                    out=torch.empty(q.shape, dtype=torch.float32, device=DEV))
+    torch.cuda.synchronize()
+    rng = np.random.default_rng(0)
+    for r in range(3):
+        qs = np.sort(rng.choice(64, 6, replace=False))
+        lens = np.array([b.ctx_host[r] - 64 + i + 1 for i in qs], dtype=np.int32)
+        ref = oracle.paged_attention(q[r, qs].cpu(), b.k_pool.cpu(), b.v_pool.cpu(),
+                                     np.repeat(b.table_host[r:r + 1], len(qs), axis=0), lens, b.scale)
+        assert_close(got[r, qs].cpu(), ref, what="row %d" % r, **TOL[torch.float32])
