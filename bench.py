@@ -190,7 +190,41 @@ def other_workloads(dev, stream):
             del run, out, steps
     res["decode_run"] = runs
     res["decode_step_graph"] = graph_step(dev, stream)
+    res["prefill_chunk"] = prefill_chunk(dev, stream)
     return res
+
+
+def prefill_chunk(dev, stream, rows=16, qlen=64):
+    """Multi-query read of a 64-query chunk at the end of every row of an
+    8B-shaped layer (lengths uniform in [512, 4096]): µs per call, K/V bytes
+    read once (HBM floor) and the causal FLOPs."""
+    import numpy as np
+    import torch
+
+    import paged_kv_cache_13_amd as pkv
+    from paged_kv_cache_13_amd import harness, synth
+
+    cfg = synth.CONFIGS["llama3_8b_layer"].replace(rows=rows, seed=7)
+    b = synth.make_batch(cfg, device=dev)
+    g = torch.Generator(device=dev).manual_seed(8)
+    q = torch.randn(rows, qlen, cfg.n_heads, cfg.head_dim, generator=g, device=dev).to(torch.bfloat16)
+    out = torch.empty_like(q)
+    ws = torch.zeros(max(pkv.workspace_size_multi(q, b.k_pool, b.block_table), 1), dtype=torch.uint8, device=dev)
+
+    def call():
+        pkv.paged_attention_multi(q, b.k_pool, b.v_pool, b.block_table, b.context_lens, b.scale, out=out,
+                                  workspace=ws)
+
+    for _ in range(3):
+        call()
+    mean, med = _timed(call, stream, 20)
+    kv = harness.read_bytes(b.ctx_host, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.block_size, 2, 2)
+    kv += (qlen - 1) * rows * cfg.n_heads * cfg.head_dim * 4  # the other queries' q and out
+    vis = sum(int(n) - qlen + i + 1 for n in b.ctx_host for i in range(qlen))
+    flops = 4 * cfg.n_heads * cfg.head_dim * vis
+    return {"rows": rows, "query_len": qlen, "sum_ctx": int(b.ctx_host.sum()), "us": round(mean, 2),
+            "us_median": round(med, 2), "GB/s_kv_once": round(kv / (mean * 1e-6) / 1e9, 1),
+            "TFLOP/s": round(flops / (mean * 1e-6) / 1e12, 2)}
 
 
 def graph_step(dev, stream, reps=100):

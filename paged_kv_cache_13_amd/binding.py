@@ -210,6 +210,17 @@ def paged_attention_into(q, k_pool, v_pool, block_table, context_lens, scale, ou
     return out
 
 
+def workspace_size_multi(q: torch.Tensor, k_pool: torch.Tensor, block_table: torch.Tensor,
+                         out_dtype: Optional[torch.dtype] = None, partition_tokens: int = 0) -> int:
+    """Workspace bytes of paged_attention_multi for q [rows, query_len, H, hd]."""
+    rows, qlen, n_heads, hd = q.shape
+    nb, nkv, bs, _ = k_pool.shape
+    d = AttnDesc(rows=rows, n_heads=n_heads, n_kv_heads=nkv, head_dim=hd, block_size=bs,
+                 max_blocks_per_row=block_table.shape[1], num_blocks=nb, dtype=_dtype_code(q),
+                 out_dtype=_DTYPES[out_dtype or q.dtype], partition_tokens=int(partition_tokens))
+    return int(load_library().pkv_paged_attention_multi_workspace_size(ctypes.byref(d), qlen))
+
+
 def paged_attention_multi(q, k_pool, v_pool, block_table, context_lens, scale, out=None,
                           workspace: Optional[torch.Tensor] = None, partition_tokens: int = 0,
                           stats: Optional["ReadCounters"] = None) -> torch.Tensor:
