@@ -68,7 +68,8 @@ typedef enum pkv_status {
   PKV_ERR_WORKSPACE = 8,     /* workspace NULL or smaller than pkv_paged_attention_workspace_size */
   PKV_ERR_PARTITION = 9,     /* partition_tokens not a positive multiple of block_size */
   PKV_ERR_LAUNCH = 10,       /* the HIP runtime refused a launch (hipGetLastError) */
-  PKV_ERR_MODE = 11          /* read counters of different reads (mode or block differ) */
+  PKV_ERR_MODE = 11,         /* read counters of different reads (mode or block differ) */
+  PKV_ERR_EXHAUSTED = 12     /* the pool has fewer free blocks than asked for */
 } pkv_status;
 
 typedef enum pkv_dtype {
@@ -248,6 +249,41 @@ int pkv_read_stats_since(const pkv_read_stats *now, const pkv_read_stats *earlie
 /* score_cells / held_cells; 1.0 when nothing is held (the gathered read
  * holds everything it is charged: its saving is 1, not "unmeasured"). */
 double pkv_read_stats_saving(const pkv_read_stats *s);
+
+/*
+ * Block allocator of the shared pool (host memory only).  ("Day 17" page,
+ * "What I added today" and "Post angle": a pool of fixed blocks handed out to
+ * sequences and taken back when they finish, free-and-reuse; running out is
+ * an error the caller sees.)  The caller owns the struct and its storage of
+ * pkv_allocator_storage_bytes(num_blocks) bytes (4-byte aligned); nothing is
+ * allocated.  Not thread-safe: one owner at a time.
+ */
+typedef struct pkv_block_allocator {
+  int32_t *free_ids;          /* stack of free block ids (inside the storage) */
+  uint8_t *in_use;            /* one byte per block (inside the storage) */
+  int64_t num_blocks, num_free;
+} pkv_block_allocator;
+
+size_t pkv_allocator_storage_bytes(int64_t num_blocks);  /* 0 if num_blocks is out of 1..2^31-1 */
+/* Every block free.  seed 0 hands out blocks 0, 1, 2, ...; any other seed a
+ * shuffled order (splitmix64 + Fisher-Yates), so tables come out fragmented. */
+int pkv_allocator_init(pkv_block_allocator *a, void *storage, size_t storage_bytes, int64_t num_blocks,
+                       uint64_t seed);
+/* Take n blocks into ids[0..n): all or nothing, PKV_ERR_EXHAUSTED if fewer
+ * than n are free. */
+int pkv_allocator_alloc(pkv_block_allocator *a, int64_t n, int32_t *ids);
+/* Give blocks back.  PKV_ERR_SHAPE, with nothing freed, if an id is out of
+ * range or not in use (a double free). */
+int pkv_allocator_free(pkv_block_allocator *a, const int32_t *ids, int64_t n);
+int64_t pkv_allocator_num_free(const pkv_block_allocator *a);
+/* Slots of `count` positions appended to a sequence of `length` positions
+ * whose block table row is table_row[0..max_blocks): blocks are taken from
+ * the allocator as the length crosses block boundaries (written into the
+ * row), then slots[i] = block * block_size + offset of position length + i.
+ * All or nothing: PKV_ERR_EXHAUSTED takes no block, PKV_ERR_SHAPE if the row
+ * would overflow max_blocks. */
+int pkv_append_slots(pkv_block_allocator *a, int32_t *table_row, int32_t max_blocks, int32_t block_size,
+                     int32_t length, int32_t count, int64_t *slots);
 
 /* Static text for a status code ("unknown status" for anything else). */
 const char *pkv_strerror(int status);

@@ -78,6 +78,18 @@ def load_library():
     lib.pkv_paged_attention_multi.restype = ctypes.c_int
     lib.pkv_paged_attention_multi_workspace_size.argtypes = [ctypes.POINTER(AttnDesc), i32]
     lib.pkv_paged_attention_multi_workspace_size.restype = sz
+    lib.pkv_allocator_storage_bytes.argtypes = [i64]
+    lib.pkv_allocator_storage_bytes.restype = sz
+    lib.pkv_allocator_init.argtypes = [vp, vp, sz, i64, ctypes.c_uint64]
+    lib.pkv_allocator_init.restype = ctypes.c_int
+    lib.pkv_allocator_alloc.argtypes = [vp, i64, vp]
+    lib.pkv_allocator_alloc.restype = ctypes.c_int
+    lib.pkv_allocator_free.argtypes = [vp, vp, i64]
+    lib.pkv_allocator_free.restype = ctypes.c_int
+    lib.pkv_allocator_num_free.argtypes = [vp]
+    lib.pkv_allocator_num_free.restype = i64
+    lib.pkv_append_slots.argtypes = [vp, vp, i32, i32, i32, i32, vp]
+    lib.pkv_append_slots.restype = ctypes.c_int
     lib.pkv_decode_step.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp, vp, vp, vp,
                                     ctypes.c_float, vp, vp, sz, vp]
     lib.pkv_decode_step.restype = ctypes.c_int
@@ -340,3 +352,62 @@ def paged_attention(q, k_pool, v_pool, block_table, context_lens, scale, out=Non
         out = torch.empty_like(q)
     return paged_attention_into(q, k_pool, v_pool, block_table, context_lens, scale, out,
                                 partition_tokens=partition_tokens, stats=stats)
+
+
+class BlockAllocatorStruct(ctypes.Structure):
+    _fields_ = [("free_ids", ctypes.c_void_p), ("in_use", ctypes.c_void_p),
+                ("num_blocks", ctypes.c_int64), ("num_free", ctypes.c_int64)]
+
+
+class KVCacheExhausted(PkvError):
+    """The pool has fewer free blocks than a call asked for."""
+
+
+class BlockAllocator:
+    """The library's block allocator of a shared pool (host memory): blocks
+    out as sequences grow, back when they finish, reused by the next ones."""
+
+    EXHAUSTED = 12
+
+    def __init__(self, num_blocks: int, seed: int = 0):
+        lib = load_library()
+        nbytes = int(lib.pkv_allocator_storage_bytes(num_blocks))
+        if nbytes == 0:
+            raise ValueError("num_blocks out of range")
+        import numpy as np
+        self._storage = np.zeros((nbytes + 3) // 4, dtype=np.int32)  # 4-byte aligned
+        self._a = BlockAllocatorStruct()
+        _check(lib.pkv_allocator_init(ctypes.byref(self._a), self._storage.ctypes.data, nbytes, num_blocks,
+                                      ctypes.c_uint64(seed)))
+
+    def _call(self, status):
+        if status == self.EXHAUSTED:
+            raise KVCacheExhausted(status, load_library().pkv_strerror(status).decode())
+        _check(status)
+
+    @property
+    def num_free(self) -> int:
+        return int(load_library().pkv_allocator_num_free(ctypes.byref(self._a)))
+
+    def allocate(self, n: int):
+        import numpy as np
+        ids = np.empty(max(n, 1), dtype=np.int32)
+        self._call(load_library().pkv_allocator_alloc(ctypes.byref(self._a), n, ids.ctypes.data))
+        return ids[:n]
+
+    def free(self, ids) -> None:
+        import numpy as np
+        ids = np.ascontiguousarray(np.asarray(ids, dtype=np.int32))
+        self._call(load_library().pkv_allocator_free(ctypes.byref(self._a), ids.ctypes.data, ids.size))
+
+    def append_slots(self, table_row, block_size: int, length: int, count: int):
+        """Slots (int64) of `count` positions appended at `length` to the
+        sequence whose block-table row `table_row` (int32 numpy, written in
+        place) is; new blocks come from this allocator."""
+        import numpy as np
+        assert table_row.dtype == np.int32 and table_row.flags.c_contiguous
+        slots = np.empty(max(count, 1), dtype=np.int64)
+        self._call(load_library().pkv_append_slots(ctypes.byref(self._a), table_row.ctypes.data,
+                                                   table_row.size, block_size, length, count,
+                                                   slots.ctypes.data))
+        return slots[:count]

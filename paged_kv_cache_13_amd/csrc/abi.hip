@@ -221,6 +221,7 @@ const char *pkv_strerror(int status) {
     case PKV_ERR_PARTITION: return "partition_tokens must be a positive multiple of block_size";
     case PKV_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
     case PKV_ERR_MODE: return "read counters of different reads (mode or block differ)";
+    case PKV_ERR_EXHAUSTED: return "the pool has fewer free blocks than asked for";
     default: return "unknown status";
   }
 }

@@ -14,7 +14,7 @@ import sys
 HERE = os.path.dirname(os.path.abspath(__file__))
 PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
-SOURCES = ["decode.hip", "scatter.hip", "abi.hip"]
+SOURCES = ["decode.hip", "scatter.hip", "abi.hip", "alloc.hip"]
 OUT = os.path.join(PKG, "libpkv.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

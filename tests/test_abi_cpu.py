@@ -30,7 +30,9 @@ def declared_functions():
 
 
 def test_header_declares_the_entry_points():
-    assert declared_functions() == ["pkv_decode_step", "pkv_paged_attention",
+    assert declared_functions() == ["pkv_allocator_alloc", "pkv_allocator_free", "pkv_allocator_init",
+                                    "pkv_allocator_num_free", "pkv_allocator_storage_bytes",
+                                    "pkv_append_slots", "pkv_decode_step", "pkv_paged_attention",
                                     "pkv_paged_attention_multi", "pkv_paged_attention_multi_workspace_size",
                                     "pkv_paged_attention_workspace_size", "pkv_read_stats_init",
                                     "pkv_read_stats_record", "pkv_read_stats_record_read",
@@ -44,7 +46,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, 12):
+    for code in range(0, 13):
         assert lib.pkv_strerror(code).decode() != "unknown status"
     assert lib.pkv_strerror(0).decode() == "ok"
     assert lib.pkv_strerror(999).decode() == "unknown status"

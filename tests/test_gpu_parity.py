@@ -5,6 +5,7 @@ cover many partitions and ragged tails; the Llama-3-8B-shaped layer is checked
 in full, the skewed long-context batch on sampled rows, both in the launch
 configuration the benchmark times (default partition length).
 """
+import math
 import sys
 
 import numpy as np
@@ -505,3 +506,75 @@ def test_multi_query_prefill_chunk_sampled():
         ref = oracle.paged_attention(q[r, qs].cpu(), b.k_pool.cpu(), b.v_pool.cpu(),
                                      np.repeat(b.table_host[r:r + 1], len(qs), axis=0), lens, b.scale)
         assert_close(got[r, qs].cpu(), ref, what="row %d" % r, **TOL[torch.float32])
+
+
+# ---------------------------------------------------------------------------
+# pool churn: sequences finish and new ones reuse their blocks under the
+# scatter + read loop (the library's allocator hands the blocks out)
+# ---------------------------------------------------------------------------
+
+def test_pool_churn_under_scatter_and_read():
+    rng = np.random.default_rng(3)
+    rows, H, KV, hd, bs, width_blocks = 12, 32, 8, 128, 16, 24
+    nb = 90  # well under rows * width_blocks: blocks are reused and the pool runs dry
+    alloc = pkv.BlockAllocator(nb, seed=17)
+    k_pool = torch.full((nb, KV, bs, hd), float("nan"), dtype=torch.bfloat16, device=DEV)
+    v_pool = torch.full((nb, KV, hd, bs), float("nan"), dtype=torch.bfloat16, device=DEV)
+    tables = np.full((rows, width_blocks), -1, dtype=np.int32)
+    lens = np.zeros(rows, dtype=np.int32)
+    g = torch.Generator(device=DEV).manual_seed(4)
+    scale = 1.0 / math.sqrt(hd)
+    finished = started = exhausted = 0
+
+    def start(r):
+        nonlocal started, exhausted
+        n = int(rng.integers(1, 200))
+        try:
+            slots = alloc.append_slots(tables[r], bs, 0, n)
+        except pkv.KVCacheExhausted:
+            exhausted += 1
+            return
+        k = torch.randn(n, KV, hd, generator=g, device=DEV).to(torch.bfloat16)
+        v = torch.randn(n, KV, hd, generator=g, device=DEV).to(torch.bfloat16)
+        pkv.reshape_and_cache(k, v, torch.from_numpy(slots).to(DEV), k_pool, v_pool)
+        lens[r] = n
+        started += 1
+
+    for r in range(rows):
+        start(r)
+    note("pool churn")
+    for step in range(120):
+        for r in range(rows):  # finish some sequences: their blocks go back to the pool
+            if lens[r] and rng.random() < 0.08:
+                alloc.free(tables[r, :-(-int(lens[r]) // bs)])
+                tables[r] = -1
+                lens[r] = 0
+                finished += 1
+        for r in range(rows):
+            if lens[r] == 0:
+                start(r)
+        # one decode step for every live row: append a token, scatter, read
+        live = np.nonzero(lens)[0]
+        slot_step = np.full(rows, -1, dtype=np.int64)
+        for r in live:
+            if lens[r] + 1 > width_blocks * bs:
+                continue
+            try:
+                slot_step[r] = alloc.append_slots(tables[r], bs, int(lens[r]), 1)[0]
+                lens[r] += 1
+            except pkv.KVCacheExhausted:
+                exhausted += 1
+        kn = torch.randn(rows, KV, hd, generator=g, device=DEV).to(torch.bfloat16)
+        vn = torch.randn(rows, KV, hd, generator=g, device=DEV).to(torch.bfloat16)
+        q = torch.randn(rows, H, hd, generator=g, device=DEV).to(torch.bfloat16)
+        table = np.where(tables >= 0, tables, 0).astype(np.int32)
+        bt = torch.from_numpy(table).to(DEV)
+        cl = torch.from_numpy(lens.copy()).to(DEV)
+        out = pkv.decode_step(q, kn, vn, torch.from_numpy(slot_step).to(DEV), k_pool, v_pool, bt, cl, scale)
+        rect = harness.gathered_rect_read(q, k_pool, v_pool, bt, cl, scale)
+        torch.cuda.synchronize()
+        assert_close(out.float().cpu(), rect.cpu(), what="churn step %d vs rect" % step, **TOL[torch.bfloat16])
+        if step % 40 == 39:
+            ref = oracle.paged_attention(q.cpu(), k_pool.cpu(), v_pool.cpu(), table, lens, scale)
+            assert_close(out.float().cpu(), ref, what="churn step %d vs oracle" % step, **TOL[torch.bfloat16])
+    assert finished > 10 and started > rows + 10 and exhausted > 0
