@@ -31,7 +31,7 @@ HBM_PEAK_GBS = 8000.0
 # a plain copy of known size (profiles/decode_stream_<workload>_hbm_counters.md),
 # valid only for the kernel sources they were taken on.
 PROFILED_TRAFFIC = {
-    "llama3_8b_layer": {"src": "9d73b45ef3ed8729", "read_bytes": 577702742},
+    "llama3_8b_layer": {"src": "6a8e55044bcbbeed", "read_bytes": 577796395},
 }
 KERNEL_SOURCES = ("decode.hip", "pkv_internal.h", "abi.hip")
 
