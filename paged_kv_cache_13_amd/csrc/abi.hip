@@ -107,11 +107,12 @@ int plan_decode(const pkv_attn_desc *d, Plan *pl) {
 }
 
 // Multi-query read: bf16, head_dim 64/128.  Partitions are whole 32-position
-// groups: the caller's partition_tokens rounded up to one, else a default
-// that fills about kTargetMultiUnits waves.
-constexpr int64_t kTargetMultiUnits = 1024;
+// groups, at most kMultiMaxPartition positions: the caller's partition_tokens
+// rounded up to a group (and capped), else a default that gives about
+// kTargetMultiWaves waves over all workgroups.
+constexpr int64_t kTargetMultiWaves = 4096;
 struct MultiPlan {
-  int32_t q_tiles, q_per_tile;
+  int32_t q_tiles, q_per_tile, q_blocks;
 };
 int plan_multi(const pkv_attn_desc *d, int32_t query_len, Plan *pl, MultiPlan *mp) {
   const int st = plan_decode(d, pl);
@@ -120,24 +121,27 @@ int plan_multi(const pkv_attn_desc *d, int32_t query_len, Plan *pl, MultiPlan *m
   if (d->head_dim != 64 && d->head_dim != 128) return PKV_ERR_HEAD_DIM;
   if (query_len < 1 || query_len > 65535) return PKV_ERR_SHAPE;
   const int32_t cap = d->max_blocks_per_row * d->block_size;
-  mp->q_per_tile = 16 / pl->group;
+  mp->q_per_tile = 32 / pl->group;  // group <= 16
   mp->q_tiles = (query_len + mp->q_per_tile - 1) / mp->q_per_tile;
+  const int32_t waves = pkv::multi_waves(mp->q_tiles);
+  mp->q_blocks = (mp->q_tiles + waves - 1) / waves;
   const int64_t g32 = pkv::kGroupPositions;
   int64_t part;
   if (d->partition_tokens) {
     part = (d->partition_tokens + g32 - 1) / g32 * g32;
   } else {
-    const int64_t tiles = (int64_t)mp->q_tiles * d->n_kv_heads * (d->rows > 0 ? d->rows : 1);
-    const int64_t want = (kTargetMultiUnits + tiles - 1) / tiles;
-    part = ((cap + want - 1) / want + g32 - 1) / g32 * g32;
+    const int64_t blocks = (int64_t)mp->q_blocks * d->n_kv_heads * (d->rows > 0 ? d->rows : 1);
+    const int64_t want_wgs = (kTargetMultiWaves / waves + blocks - 1) / blocks;
+    part = ((cap + want_wgs - 1) / want_wgs + g32 - 1) / g32 * g32;
     if (part > kDefaultPartition) part = kDefaultPartition;
   }
+  if (part > pkv::kMultiMaxPartition) part = pkv::kMultiMaxPartition;
   if (part < g32) part = g32;
   const int64_t cap32 = (cap + g32 - 1) / g32 * g32;
   if (part > cap32) part = cap32;
   pl->partition = (int32_t)part;
   pl->max_parts = (int32_t)((cap + part - 1) / part);
-  const int64_t units = (int64_t)pl->max_parts * mp->q_tiles * d->n_kv_heads * d->rows;
+  const int64_t units = (int64_t)pl->max_parts * mp->q_blocks * d->n_kv_heads * d->rows;
   const int64_t vrows = (int64_t)d->rows * query_len;
   if (units > INT_MAX || vrows * d->n_heads > INT_MAX) return PKV_ERR_SHAPE;
   pl->stream = 0;
@@ -330,6 +334,7 @@ int pkv_paged_attention_multi(const pkv_attn_desc *d, int32_t query_len, const v
   a.query_len = query_len;
   a.q_tiles = mp.q_tiles;
   a.q_per_tile = mp.q_per_tile;
+  a.q_blocks = mp.q_blocks;
   return pkv::launch_multi(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 

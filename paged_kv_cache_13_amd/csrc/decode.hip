@@ -23,6 +23,8 @@
 // consecutive rows.  Dot products are reduced across those LPT lanes with DPP
 // row permutes.  Scores are kept in the log2 domain (scale * log2 e folded in)
 // so the exponentials are v_exp_f32.
+#include <climits>
+
 #include "pkv_internal.h"
 
 namespace pkv {
@@ -425,6 +427,7 @@ __global__ __launch_bounds__(128) void decode_merge(DecodeArgs a) {
 // ---------------------------------------------------------------------------
 typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
 typedef float f32x4_t __attribute__((ext_vector_type(4)));
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
 
 // All-reduce over the four 16-lane rows (lane bits 4 and 5).  Written with
 // ds_bpermute exchanges: this compiler folds the two results of a
@@ -1164,6 +1167,9 @@ __global__ __launch_bounds__(256) void decode_stream_merge(DecodeArgs a) {
 // are reused (block ids, q, partials); the streaming hint lifts the
 // sustained read rate of 4 KiB tile gathers by about 14% on MI355X.
 constexpr int kStreamingLoad = 2;  // the nt bit of the cache-policy operand
+// The multi-query read's staging loads take the default cache policy: a
+// non-temporal hint measured slower there.
+constexpr int kMultiLoadPolicy = 0;
 
 template <int HD, int BS>
 __device__ __forceinline__ void stage_group(uint4 *s_k, uint4 *s_v, const DecodeArgs &a, const Cursor &c,
@@ -1357,159 +1363,462 @@ hipError_t launch_dt(const DecodeArgs &a, hipStream_t s) {
 // query_len positions (already in the pool), causal inside the chunk -- query
 // i at position n - query_len + i sees positions 0 .. n - query_len + i.
 //
-// The 16 columns of the score tile S^T = K Q^T hold (query, head) pairs:
-// 16 / group queries of one kv head's group per tile.  One wave per
-// (position partition, query tile, kv head, row) walks its partition's
-// 32-position groups -- only those some query of the tile can see -- with the
-// same LDS-staged K/V and MFMA tiles as the one-query read, a per-column
-// causal bound on the scores, and an online softmax that tolerates a column
-// with nothing visible yet.  Rows of one partition are written directly;
-// longer rows leave per-partition (max, sum, acc) for decode_multi_merge.
+// Matrix-core layout (v_mfma_f32_32x32x16_bf16, which on gfx950 sustains
+// twice the rate of the 16x16x32 shape):
+//   scores  S^T[32 positions][32 columns] = K Q^T, hd in k-steps of 16;
+//   output  O^T[32 hd][32 columns] += V^T P^T, positions in k-steps of 16.
+// A column is a (query, head) pair: 32 / group queries of one kv head's group
+// per tile.  Row m of the score tile holds position sigma(m) of the group,
+// chosen so that the 16 scores a lane receives are, in register order, the
+// 16 positions it must supply as its P operand (8 per k-step): lane half h
+// gets positions 8h .. 8h+7 and 16+8h .. 16+8h+7.  The softmax therefore
+// needs no data movement between the two products, and a column's max is
+// one exchange between lanes l and l ^ 32.
+//
+// A workgroup of NW waves serves one (position partition, query block, kv
+// head, row); wave w owns one 32-column tile, so a block covers NW * 32 /
+// group queries and every K/V byte staged for the block feeds all of them.
+// The 32-position groups of the partition (only those some query of the
+// block can see) go through a ring of multi_ring(NW) LDS group buffers
+// filled by direct-to-LDS loads, each wave loading its share of every group.
+// Groups are consumed two per step: one barrier per step publishes the pair
+// and frees the pair before it for refilling.  Rows of one partition are
+// written directly; longer rows leave per-partition (max, sum, acc) for
+// decode_multi_merge.
 // ---------------------------------------------------------------------------
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+
+// Position (0..31, within the group) of score-tile row m.
+__device__ __forceinline__ int multi_row_pos(int m) {
+  const int a = m >> 3, b = (m >> 2) & 1, c = m & 3;
+  return 16 * (a >> 1) + 8 * b + 4 * (a & 1) + c;
+}
+
+// K of a staged group is kept as it lies in the pool: K slot s is the
+// contiguous 1 KB of positions RPS s .. RPS s + RPS - 1 (RPS = 64 / CPR rows
+// of CPR = head_dim / 8 16-byte chunks), so every load reads whole cache
+// lines.  Within a slot, chunk `col` of row p (group-relative position) sits
+// at chunk CPR (p % RPS) + (col ^ kswz(p)): the XOR spreads the 16 lanes of
+// one fragment read over distinct LDS banks.
 template <int HD>
-__device__ __forceinline__ void group_softmax_pv_causal(const f32x4_t (&sacc)[2], bf16x8_t (&v)[HD / 16],
-                                                        f32x4_t *acc, float &m, float &l, float c, int col_end,
-                                                        int row_end, int gbase, int lg) {
-  constexpr int DT = HD / 16;
-  const int tl = gbase + 8 * lg;
-  float s[8];
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-    for (int j = 0; j < 4; ++j) s[4 * tt + j] = (tl + 4 * tt + j < col_end) ? sacc[tt][j] * c : -INFINITY;
-  float mx = fmaxf(fmaxf(fmaxf(s[0], s[1]), fmaxf(s[2], s[3])), fmaxf(fmaxf(s[4], s[5]), fmaxf(s[6], s[7])));
-  mx = max_across_rows(mx);
-  const float m_new = fmaxf(m, mx);
-  const float alpha = (m == m_new) ? 1.f : exp2_fast(m - m_new);
-  m = m_new;
-  float pv[8], psum = 0.f;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    pv[e] = s[e] == -INFINITY ? 0.f : exp2_fast(s[e] - m_new);  // nothing visible yet: m_new is -inf too
-    psum += pv[e];
+__device__ __forceinline__ int kswz(int p) {
+  return HD == 128 ? (p & 15) : ((p >> 1) & 7);
+}
+
+// LDS uint4 index, within a staged group, of this lane's K fragment for
+// k-step ks: position sigma(lane % 32), hd 16 ks + 8 (lane / 32) .. + 8.
+template <int HD>
+__device__ __forceinline__ int multi_kfrag(int ks, int lane) {
+  constexpr int CPR = HD / 8, RPS = 64 / CPR;
+  const int p = multi_row_pos(lane & 31), col = 2 * ks + (lane >> 5);
+  return (p / RPS) * kWave + CPR * (p % RPS) + (col ^ kswz<HD>(p));
+}
+
+// Four entries of an LDS int table, read and waited for in one asm block.
+// The compiler's wait insertion cannot tell these reads from the
+// direct-to-LDS loads still in flight into the ring buffers, and would drain
+// all of those first; the table is written once, before a barrier, and never
+// by a direct-to-LDS load.
+__device__ __forceinline__ void lds_read4(const int32_t *table, int i0, int i1, int i2, int i3, int32_t &x0,
+                                          int32_t &x1, int32_t &x2, int32_t &x3) {
+  const __attribute__((address_space(3))) int32_t *t = (const __attribute__((address_space(3))) int32_t *)table;
+  const uint32_t a0 = (uint32_t)(uintptr_t)(t + i0), a1 = (uint32_t)(uintptr_t)(t + i1),
+                 a2 = (uint32_t)(uintptr_t)(t + i2), a3 = (uint32_t)(uintptr_t)(t + i3);
+  asm volatile(
+      "ds_read_b32 %0, %4\n\t"
+      "ds_read_b32 %1, %5\n\t"
+      "ds_read_b32 %2, %6\n\t"
+      "ds_read_b32 %3, %7\n\t"
+      "s_waitcnt lgkmcnt(0)"
+      : "=&v"(x0), "=&v"(x1), "=&v"(x2), "=&v"(x3)
+      : "v"(a0), "v"(a1), "v"(a2), "v"(a3)
+      : "memory");
+}
+
+// Block id of the j-th block a group touches (j < 32 / BS), by selects.
+template <int BS>
+__device__ __forceinline__ size_t group_block(int j, int32_t id0, int32_t id1, int32_t id2, int32_t id3) {
+  int32_t b = id0;
+  if constexpr (BS < 32) b = j >= 1 ? id1 : b;
+  if constexpr (BS < 16) {
+    b = j >= 2 ? id2 : b;
+    b = j >= 3 ? id3 : b;
   }
-  l = l * alpha + psum;
-  if (__any(alpha != 1.f)) {
+  return (size_t)b;
+}
+
+// Stage one group: this wave's share of the NSLOT 1 KB slots.  K slots are
+// contiguous runs of the K tile (see kswz); V slot (dt, kk): lane l loads hd
+// row 32 dt + l % 32, positions 16 kk + 8 (l / 32) .. + 8 (one 16-byte run of
+// the dimension-major V tile).  Positions past `last` read position `last`.
+template <int HD, int BS, int NW>
+__device__ __forceinline__ void stage_multi(uint4 *st, const DecodeArgs &a, const int32_t *s_blk, int blk0, int nblk,
+                                            int kvh, int t0, int last, int wave, int lane) {
+  constexpr int KS = HD / 16, NSLOT = HD / 8, SPW = NSLOT / NW, CPR = HD / 8, RPS = 64 / CPR;
+  constexpr int LOG2_BS = BS == 8 ? 3 : (BS == 16 ? 4 : 5);
+  constexpr int bmask = BS - 1;
+  const int lr = lane & 31, h = lane >> 5;
+  // the group's (up to four) block ids, the same for every lane
+  const int gb = (t0 >> LOG2_BS) - blk0;
+  int32_t id0, id1, id2, id3;
+  lds_read4(s_blk, gb, min(gb + 1, nblk - 1), min(gb + 2, nblk - 1), min(gb + 3, nblk - 1), id0, id1, id2, id3);
+  const int tb0 = t0 >> LOG2_BS;
+  const int tv0 = min(t0 + 8 * h, last) & ~7, tv1 = min(t0 + 16 + 8 * h, last) & ~7;
+  const size_t bv0 = group_block<BS>((tv0 >> LOG2_BS) - tb0, id0, id1, id2, id3);
+  const size_t bv1 = group_block<BS>((tv1 >> LOG2_BS) - tb0, id0, id1, id2, id3);
+  const char *vp0 = static_cast<const char *>(a.v_pool) +
+                    ((((bv0 * a.n_kv_heads + kvh) * HD + lr) << LOG2_BS) + (tv0 & bmask)) * 2;
+  const char *vp1 = static_cast<const char *>(a.v_pool) +
+                    ((((bv1 * a.n_kv_heads + kvh) * HD + lr) << LOG2_BS) + (tv1 & bmask)) * 2;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) acc[dt] *= alpha;
-  }
-  uint32_t hw[4], lw[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t h0 = bf16_bits_rne(pv[2 * i]), h1 = bf16_bits_rne(pv[2 * i + 1]);
-    const float r0 = pv[2 * i] - __builtin_bit_cast(float, h0 << 16);
-    const float r1 = pv[2 * i + 1] - __builtin_bit_cast(float, h1 << 16);
-    hw[i] = h0 | (h1 << 16);
-    lw[i] = bf16_bits_rne(r0) | (bf16_bits_rne(r1) << 16);
-  }
-  const bf16x8_t phi = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
-  const bf16x8_t plo = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
-  if (gbase + 32 > row_end) {  // positions past the row end: zero their (possibly NaN) V
-    int nv = row_end - tl;
-    nv = nv < 0 ? 0 : (nv > 8 ? 8 : nv);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) v[dt] = keep_first(v[dt], nv);
-  }
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) {
-    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v[dt], phi, acc[dt], 0, 0, 0);
-    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(v[dt], plo, acc[dt], 0, 0, 0);
+  for (int x = 0; x < SPW; ++x) {
+    const int s = wave + NW * x;  // wave-uniform slot
+    const char *src;
+    if (s < KS) {
+      const int p = RPS * s + lane / CPR, t = min(t0 + p, last);
+      const int col = (lane % CPR) ^ kswz<HD>(p);
+      const size_t bk = group_block<BS>((t >> LOG2_BS) - tb0, id0, id1, id2, id3);
+      src = static_cast<const char *>(a.k_pool) + ((((bk * a.n_kv_heads + kvh) << LOG2_BS) + (t & bmask)) * HD + 8 * col) * 2;
+    } else {
+      const int v = s - KS;  // hd tile v / 2, position run v % 2
+      src = ((v & 1) ? vp1 : vp0) + (size_t)(v >> 1) * (32 * BS * 2);
+    }
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)src,
+                                     (void __attribute__((address_space(3))) *)(st + s * kWave), 16, 0,
+                                     kMultiLoadPolicy);
   }
 }
 
-template <int HD, int BS>
-__global__ __launch_bounds__(kWave) void decode_multi(DecodeArgs a) {
-  constexpr int KS = HD / 32, DT = HD / 16;
-  __shared__ uint4 s_k[2 * KS * kWave];
-  __shared__ uint4 s_v[DT * kWave];
-  const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
+// s_waitcnt immediate for vmcnt(n) and lgkmcnt(0) (expcnt left alone).
+__host__ __device__ constexpr int vmcnt_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
+
+// Until at most `ahead` (0 .. R - 4) later groups of this wave's staging
+// loads (SPW each) are in flight, and every LDS read of this wave has
+// returned.  s_waitcnt takes an immediate: one case per count.
+template <int SPW, int R>
+__device__ __forceinline__ void wait_ring(int ahead) {
+  static_assert(R == 4 || R == 8, "ring of 4 or 8 groups");
+  if constexpr (R == 8) {
+    if (ahead >= 4) { __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(4 * SPW)); return; }
+    if (ahead == 3) { __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(3 * SPW)); return; }
+    if (ahead == 2) { __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(2 * SPW)); return; }
+    if (ahead == 1) { __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(SPW)); return; }
+  }
+  __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
+}
+
+// Per-wave state of the multi-query read: this lane's column and its
+// softmax state.  acc[dt] register j is output hd 32 dt + 8 (j / 4) +
+// 4 (lane / 32) + j % 4 of the column.
+template <int HD>
+struct MultiState {
+  bf16x8_t qb[HD / 16];  // q of the column, hd 16 ks + 8 (lane / 32) .. + 8
+  int col_end;           // positions the column sees (INT_MAX: not a query)
+  int min_end;           // wave-uniform: the least col_end of a query in the tile
+  float m, l;            // reference max (log2 units) and this lane's part of the sum
+  f32x16_t acc[HD / 32];
+};
+
+// Headroom, in log2 units, of the lazy rescaling: a column's reference max
+// moves only when a group's max exceeds it by more than this, so its weights
+// stay below 2^8 and the accumulators are rescaled for a few groups of a
+// partition rather than for most of them.  The result is the same softmax:
+// numerator and denominator share the reference.
+constexpr float kLazyRescale = 8.f;
+
+// 8 weights as RNE bf16 hi + lo pairs, packed for the B operand of the P.V
+// product (hi + lo carries 16 significant bits).
+__device__ __forceinline__ void split_bf16_hi_lo(const float *p, bf16x8_t &phi, bf16x8_t &plo) {
+  uint32_t hw[4], lw[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const f32x2_t v = {p[2 * i], p[2 * i + 1]};
+    const uint32_t hb = __builtin_bit_cast(uint32_t, __builtin_convertvector(v, bf16x2_t));
+    const f32x2_t r = {p[2 * i] - __builtin_bit_cast(float, hb << 16),
+                       p[2 * i + 1] - __builtin_bit_cast(float, hb & 0xFFFF0000u)};
+    hw[i] = hb;
+    lw[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(r, bf16x2_t));
+  }
+  phi = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
+  plo = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+}
+
+// Raw scores of one group for the softmax statistics: register j holds
+// position gbase + 16 (j / 8) + 8 h + j % 8.  Where the causal bound of some
+// column falls in the group, positions the lane's column does not see become
+// -inf; a group past the partition's last (`live` false) is all -inf.
+template <int HD>
+__device__ __forceinline__ void multi_raw(float (&raw)[16], const f32x16_t &sacc, const MultiState<HD> &S, int gbase,
+                                          int h, bool live) {
+#pragma unroll
+  for (int j = 0; j < 16; ++j) raw[j] = sacc[j];
+  if (!live || gbase + kGroupPositions > S.min_end) {
+    const int lim = live ? S.col_end - gbase - 8 * h : 0;  // register j is seen iff 16 (j / 8) + j % 8 < lim
+#pragma unroll
+    for (int j = 0; j < 16; ++j) raw[j] = 16 * (j >> 3) + (j & 7) < lim ? raw[j] : -INFINITY;
+  }
+}
+
+// V of one staged group, positions past the row end zeroed (they may hold
+// NaN): vc[dt][kk] is hd rows 32 dt .., positions 16 kk + 8 h .. + 8.
+template <int HD>
+__device__ __forceinline__ void multi_v(bf16x8_t (&vc)[HD / 32][2], const uint4 *buf, int gbase, int n, int lane) {
+  constexpr int KS = HD / 16, DT = HD / 32;
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) vc[dt][kk] = __builtin_bit_cast(bf16x8_t, buf[(KS + 2 * dt + kk) * kWave + lane]);
+  if (gbase + kGroupPositions > n) {
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk) {
+      const int nv = min(max(n - (gbase + 16 * kk + 8 * (lane >> 5)), 0), 8);
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt) vc[dt][kk] = keep_first(vc[dt][kk], nv);
+    }
+  }
+}
+
+// Groups k and k + 1 of the multi-query read (k even; k + 1 may lie past
+// the partition's last group), from a ring of R group buffers.  Wait for
+// both and publish them -- the barrier also says every wave is done with
+// groups k - 2 and k - 1, whose buffers are then refilled with groups
+// k + R - 2 and k + R - 1 -- then the scores
+// of both groups (two independent MFMA chains), one softmax update over
+// their 64 positions (one max exchange, one rescale check) and the P.V
+// products.  The ring's buffers are separate LDS arrays and each step names
+// its four statically, so the compiler can tell the reads of these groups
+// from the loads in flight into the others.
+template <int HD, int BS, int NW, int R>
+__device__ __forceinline__ void multi_pair(MultiState<HD> &S, const uint4 *c0, const uint4 *c1, uint4 *r0, uint4 *r1,
+                                           const DecodeArgs &a, const int32_t *s_blk, int blk0, int nblk, int kvh, int g0,
+                                           int k, int ng, int n, float cscale, bool active, int wave, int lane) {
+  constexpr int KS = HD / 16, DT = HD / 32, SPW = HD / 8 / NW;
+  // this wave's loads of groups k, k + 1 have landed; those of up to R - 4
+  // later groups may stay in flight
+  wait_ring<SPW, R>(min(ng - 2 - k, R - 4));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  if (k + R - 2 < ng)
+    stage_multi<HD, BS, NW>(r0, a, s_blk, blk0, nblk, kvh, (g0 + k + R - 2) * kGroupPositions, n - 1, wave, lane);
+  if (k + R - 1 < ng)
+    stage_multi<HD, BS, NW>(r1, a, s_blk, blk0, nblk, kvh, (g0 + k + R - 1) * kGroupPositions, n - 1, wave, lane);
+  if (!active) return;
+  const int h = lane >> 5;
+  const bool two = k + 1 < ng;
+  const int gb0 = (g0 + k) * kGroupPositions, gb1 = gb0 + kGroupPositions;
+  // scores of both groups, k-step outermost: two independent chains (the
+  // second group's is discarded when it does not exist)
+  f32x16_t sc0, sc1;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) sc0[j] = sc1[j] = 0.f;
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const int kf = multi_kfrag<HD>(ks, lane);
+    sc0 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, c0[kf]), S.qb[ks], sc0, 0, 0, 0);
+    sc1 = __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8_t, c1[kf]), S.qb[ks], sc1, 0, 0, 0);
+  }
+  float raw0[16], raw1[16];
+  multi_raw<HD>(raw0, sc0, S, gb0, h, true);
+  multi_raw<HD>(raw1, sc1, S, gb1, h, two);
+  // c > 0: the column max of the raw dot products, times c, is the max of
+  // its scores
+  float mx = fmaxf(raw0[0], raw1[0]);
+#pragma unroll
+  for (int j = 1; j < 16; ++j) mx = fmaxf(mx, fmaxf(raw0[j], raw1[j]));
+  mx = fmaxf(mx, __shfl_xor(mx, 32));
+  const float mxs = mx * cscale;  // -inf when the column sees nothing here
+  const bool up = mxs > S.m + kLazyRescale;
+  if (__any(up)) {  // move the reference max of the columns that outgrew it
+    const float alpha = up ? exp2_fast(S.m - mxs) : 1.f;  // 0 from -inf
+    S.m = up ? mxs : S.m;
+    S.l *= alpha;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) S.acc[dt] *= alpha;
+  }
+  // Weights (below 2^kLazyRescale), this lane's part of the row sum, hi/lo
+  // split, then the P.V products.  A -inf score gives weight 0; a column that
+  // has seen nothing yet takes 0 as its reference.
+  const float mref = S.m == -INFINITY ? 0.f : S.m;
+  float p0[16], p1[16];
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    p0[j] = exp2_fast(fmaf(raw0[j], cscale, -mref));
+    p1[j] = exp2_fast(fmaf(raw1[j], cscale, -mref));
+  }
+  float ps = 0.f;
+#pragma unroll
+  for (int j = 0; j < 16; j += 2) ps += (p0[j] + p0[j + 1]) + (p1[j] + p1[j + 1]);
+  S.l += ps;
+  bf16x8_t phi0[2], plo0[2], phi1[2], plo1[2];
+  split_bf16_hi_lo(p0, phi0[0], plo0[0]);
+  split_bf16_hi_lo(p0 + 8, phi0[1], plo0[1]);
+  split_bf16_hi_lo(p1, phi1[0], plo1[0]);
+  split_bf16_hi_lo(p1 + 8, phi1[1], plo1[1]);
+  bf16x8_t vc[DT][2];
+  multi_v<HD>(vc, c0, gb0, n, lane);
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      S.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc[dt][kk], phi0[kk], S.acc[dt], 0, 0, 0);
+#pragma unroll
+  for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt)
+      S.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc[dt][kk], plo0[kk], S.acc[dt], 0, 0, 0);
+  if (two) {
+    multi_v<HD>(vc, c1, gb1, n, lane);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        S.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc[dt][kk], phi1[kk], S.acc[dt], 0, 0, 0);
+#pragma unroll
+    for (int kk = 0; kk < 2; ++kk)
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+        S.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc[dt][kk], plo1[kk], S.acc[dt], 0, 0, 0);
+  }
+}
+
+template <int HD, int BS, int NW>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(NW / 4 > 1 ? NW / 4 : 1, 2))) void
+decode_multi(DecodeArgs a) {
+  constexpr int KS = HD / 16, DT = HD / 32, NSLOT = HD / 8;
+  static_assert(NSLOT % NW == 0, "every wave stages the same number of slots");
+  constexpr int R = multi_ring(NW);  // group buffers in the ring
+  constexpr int STAGE = NSLOT * kWave;  // uint4 per staged group
+  constexpr int LOG2_BS = BS == 8 ? 3 : (BS == 16 ? 4 : 5);
+  __shared__ uint4 s_b0[STAGE], s_b1[STAGE], s_b2[STAGE], s_b3[STAGE];
+  __shared__ uint4 s_b4[R > 4 ? STAGE : 1], s_b5[R > 4 ? STAGE : 1], s_b6[R > 4 ? STAGE : 1], s_b7[R > 4 ? STAGE : 1];
+  __shared__ int32_t s_blk[kMultiMaxPartition / 8];
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, kept in a scalar
+  const int lane = threadIdx.x & (kWave - 1), lr = lane & 31, h = lane >> 5;
   const int G = a.group, Q = a.query_len, QB = a.q_per_tile, P = a.partition_tokens;
-  long long u = blockIdx.x;  // kv head fastest (spread over XCDs), then row, query tile, partition
+  long long u = blockIdx.x;  // kv head fastest (spread over XCDs), then row, query block, partition
   const int kvh = (int)(u % a.n_kv_heads);
   u /= a.n_kv_heads;
   const int r = (int)(u % a.rows);
   u /= a.rows;
-  const int qt = (int)(u % a.q_tiles);
-  const int part = (int)(u / a.q_tiles);
+  const int qblk = (int)(u % a.q_blocks);
+  const int part = (int)(u / a.q_blocks);
   const int cap = a.max_blocks_per_row * a.block_size;
-  int n = a.context_lens[r];
-  n = n < 0 ? 0 : (n > cap ? cap : n);
+  const int pos0 = part * P;  // < cap: part < max_parts
+  const int blk0 = pos0 >> LOG2_BS;  // pos0 is a multiple of the block size
+  // Start-up: the row length, the partition's slice of the block table (all
+  // of it up to the table's width, whatever the length) and this lane's q
+  // are independent loads, issued together.
+  const int n_raw = a.context_lens[r];
+  const int nblk_all = (min(pos0 + P, cap) - pos0) >> LOG2_BS;
+  int32_t btab[kMultiMaxPartition / 8 / (NW * kWave) + 1];
+#pragma unroll
+  for (int x = 0; x * NW * kWave < kMultiMaxPartition / 8; ++x) {
+    const int i = threadIdx.x + x * NW * kWave;
+    btab[x] = i < nblk_all ? a.block_table[(size_t)r * a.max_blocks_per_row + blk0 + i] : 0;
+  }
+  // this lane's column: query q0 + lr / G, head kvh * G + lr % G of tile `wave`
+  MultiState<HD> S;
+  const int q_first = qblk * NW * QB;
+  const int q0 = q_first + wave * QB;
+  const int qi = q0 + lr / G, hi = lr % G;
+  const bool colv = lr < QB * G && qi < Q;
+  const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;  // fold a negative scale into q (exact)
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) {
+    const bf16x8_t x = colv ? ld_bf16x8(a.q, ((((size_t)r * Q + qi) * a.n_heads + kvh * G + hi) * HD + 16 * ks + 8 * h) * 2)
+                            : zero_bf16x8();
+    uint4 w = __builtin_bit_cast(uint4, x);
+    w.x ^= qsign;
+    w.y ^= qsign;
+    w.z ^= qsign;
+    w.w ^= qsign;
+    S.qb[ks] = __builtin_bit_cast(bf16x8_t, w);
+  }
+  const int n = n_raw < 0 ? 0 : (n_raw > cap ? cap : n_raw);
   const int nparts = n > 0 ? (n + P - 1) / P : 1;
-  if (part >= nparts) return;
-  // this lane's column: query qi, head kvh * G + hi
-  const int qi = qt * QB + lr / G, hi = lr % G;
-  const bool col = lr < QB * G && qi < Q;
-  const int col_end = col ? max(n - Q + qi + 1, 0) : 0;  // positions this query sees
-  const int q_last = min(Q - 1, qt * QB + QB - 1);
-  const int pos0 = part * P;
-  const int unit_end = max(min(pos0 + P, n - Q + q_last + 1), pos0);  // some query sees positions below
-  bf16x8_t qb[KS];
+  if (part >= nparts) return;  // the whole workgroup
+  const int q_last = min(Q - 1, q_first + NW * QB - 1);
+  const int unit_end = max(min(pos0 + P, n - Q + q_last + 1), pos0);  // some query of the block sees below
+  const int g0 = pos0 / kGroupPositions, ng = (unit_end + kGroupPositions - 1) / kGroupPositions - g0;
+  const int64_t nb1 = a.num_blocks - 1;
 #pragma unroll
-  for (int i = 0; i < KS; ++i)
-    qb[i] = col ? ld_bf16x8(a.q, ((((size_t)r * Q + qi) * a.n_heads + kvh * G + hi) * HD + (4 * i + lg) * 8) * 2)
-                : zero_bf16x8();
-  const float cscale = a.scale * kLog2e;
-  float m = -INFINITY, l = 0.f;
-  f32x4_t acc[DT];
+  for (int x = 0; x * NW * kWave < kMultiMaxPartition / 8; ++x) {
+    const int i = threadIdx.x + x * NW * kWave;
+    if (i < nblk_all) s_blk[i] = btab[x] < 0 ? 0 : (btab[x] > nb1 ? (int32_t)nb1 : btab[x]);
+  }
+  S.col_end = colv ? max(n - Q + qi + 1, 0) : INT_MAX;
+  S.min_end = q0 < Q ? max(n - Q + q0 + 1, 0) : INT_MAX;
+  S.m = -INFINITY;
+  S.l = 0.f;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-  const int g0 = pos0 / kGroupPositions, g1 = (unit_end + kGroupPositions - 1) / kGroupPositions;
-  Cursor c;
-  c.kvh = kvh;
-  c.r = r;
-  c.n = n;
-  GroupIds ids1;
-  if (g0 < g1) {
-    c.j = g0;
-    const GroupIds ids0 = load_ids<BS>(a, c, lr, lg);
-    stage_group<HD, BS>(s_k, s_v, a, c, ids0, lane, lr, lg);
-    if (g0 + 1 < g1) {
-      c.j = g0 + 1;
-      ids1 = load_ids<BS>(a, c, lr, lg);
+  for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+    for (int j = 0; j < 16; ++j) S.acc[dt][j] = 0.f;
+  const bool active = q0 < Q;  // some column of this wave is a query
+  __syncthreads();  // s_blk is written
+  const int last = n - 1;
+  // prologue: the first R - 2 groups
+  auto stage = [&](uint4 *buf, int j) {
+    if (j < ng) stage_multi<HD, BS, NW>(buf, a, s_blk, blk0, nblk_all, kvh, (g0 + j) * kGroupPositions, last, wave, lane);
+  };
+  stage(s_b0, 0);
+  stage(s_b1, 1);
+  if constexpr (R == 8) {
+    stage(s_b2, 2);
+    stage(s_b3, 3);
+    stage(s_b4, 4);
+    stage(s_b5, 5);
+  }
+  // c > 0 for the statistics; a zero scale becomes 1e-30 (every weight still
+  // exp2(0) = 1) and a NaN scale stays NaN
+  const float cs = fabsf(a.scale) * kLog2e;
+  const float cscale = cs < 1e-30f ? 1e-30f : cs;
+  if constexpr (R == 8) {
+    for (int k = 0; k < ng; k += 8) {
+      multi_pair<HD, BS, NW, R>(S, s_b0, s_b1, s_b6, s_b7, a, s_blk, blk0, nblk_all, kvh, g0, k, ng, n, cscale, active, wave,
+                                lane);
+      if (k + 2 >= ng) break;
+      multi_pair<HD, BS, NW, R>(S, s_b2, s_b3, s_b0, s_b1, a, s_blk, blk0, nblk_all, kvh, g0, k + 2, ng, n, cscale, active,
+                                wave, lane);
+      if (k + 4 >= ng) break;
+      multi_pair<HD, BS, NW, R>(S, s_b4, s_b5, s_b2, s_b3, a, s_blk, blk0, nblk_all, kvh, g0, k + 4, ng, n, cscale, active,
+                                wave, lane);
+      if (k + 6 >= ng) break;
+      multi_pair<HD, BS, NW, R>(S, s_b6, s_b7, s_b4, s_b5, a, s_blk, blk0, nblk_all, kvh, g0, k + 6, ng, n, cscale, active,
+                                wave, lane);
+    }
+  } else {
+    for (int k = 0; k < ng; k += 4) {
+      multi_pair<HD, BS, NW, R>(S, s_b0, s_b1, s_b2, s_b3, a, s_blk, blk0, nblk_all, kvh, g0, k, ng, n, cscale, active, wave,
+                                lane);
+      if (k + 2 >= ng) break;
+      multi_pair<HD, BS, NW, R>(S, s_b2, s_b3, s_b0, s_b1, a, s_blk, blk0, nblk_all, kvh, g0, k + 2, ng, n, cscale, active,
+                                wave, lane);
     }
   }
-  bf16x8_t kc[2][KS], vc[DT];
-  for (int g = g0; g < g1; ++g) {
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the staged group has landed (LDS DMA is not ordered for us)
-    asm volatile("" ::: "memory");
-#pragma unroll
-    for (int tt = 0; tt < 2; ++tt)
-#pragma unroll
-      for (int i = 0; i < KS; ++i) kc[tt][i] = __builtin_bit_cast(bf16x8_t, s_k[(tt * KS + i) * kWave + lane]);
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) vc[dt] = __builtin_bit_cast(bf16x8_t, s_v[dt * kWave + lane]);
-    __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the buffer may be refilled
-    asm volatile("" ::: "memory");
-    if (g + 1 < g1) {
-      c.j = g + 1;
-      stage_group<HD, BS>(s_k, s_v, a, c, ids1, lane, lr, lg);
-      if (g + 2 < g1) {
-        c.j = g + 2;
-        ids1 = load_ids<BS>(a, c, lr, lg);
-      }
-    }
-    f32x4_t sacc[2];
-    group_scores<HD>(kc, qb, sacc);
-    group_softmax_pv_causal<HD>(sacc, vc, acc, m, l, cscale, col_end, n, g * kGroupPositions, lg);
-  }
-  const float lt = sum_across_rows(l);
-  if (!col) return;
+  const float lt = S.l + __shfl_xor(S.l, 32);
+  if (!colv) return;
   const size_t vrow_head = ((size_t)r * Q + qi) * a.n_heads + kvh * G + hi;
   if (nparts == 1) {
     const float inv = lt > 0.f ? 1.f / lt : 0.f;  // a query before the history reads zeros
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
 #pragma unroll
-      for (int e = 0; e < 4; ++e) store_out(a.out, a.out_dtype, vrow_head * HD + 16 * dt + 4 * lg + e, acc[dt][e] * inv);
+      for (int j = 0; j < 16; ++j)
+        store_out(a.out, a.out_dtype, vrow_head * HD + 32 * dt + 8 * (j >> 2) + 4 * h + (j & 3), S.acc[dt][j] * inv);
   } else {
     const WsLayout W = ws_layout(a.rows * Q, a.n_heads, a.max_parts, HD);
     const size_t slot = vrow_head * a.max_parts + part;
     float *accp = a.ws + W.acc_off + slot * HD;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4_t *>(accp + 16 * dt + 4 * lg) = acc[dt];
-    if (lg == 0) {
-      a.ws[W.m_off + slot] = m;
+    for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+      for (int q4 = 0; q4 < 4; ++q4)
+        *reinterpret_cast<f32x4_t *>(accp + 32 * dt + 8 * q4 + 4 * h) =
+            f32x4_t{S.acc[dt][4 * q4], S.acc[dt][4 * q4 + 1], S.acc[dt][4 * q4 + 2], S.acc[dt][4 * q4 + 3]};
+    if (h == 0) {
+      a.ws[W.m_off + slot] = S.m;
       a.ws[W.l_off + slot] = lt;
     }
   }
@@ -1546,15 +1855,23 @@ __global__ __launch_bounds__(128) void decode_multi_merge(DecodeArgs a) {
   }
 }
 
-template <int HD, int BS>
+template <int HD, int BS, int NW>
 hipError_t launch_multi_t(const DecodeArgs &a, hipStream_t stream) {
-  const long long units = (long long)a.max_parts * a.q_tiles * a.rows * a.n_kv_heads;
-  hipLaunchKernelGGL((decode_multi<HD, BS>), dim3((unsigned)units), dim3(kWave), 0, stream, a);
+  const long long units = (long long)a.max_parts * a.q_blocks * a.rows * a.n_kv_heads;
+  hipLaunchKernelGGL((decode_multi<HD, BS, NW>), dim3((unsigned)units), dim3(NW * kWave), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
   hipLaunchKernelGGL(decode_multi_merge, dim3((unsigned)((size_t)a.rows * a.query_len * a.n_heads)), dim3(128), 0,
                      stream, a);
   return hipGetLastError();
+}
+
+template <int HD, int BS>
+hipError_t launch_multi_shape(const DecodeArgs &a, hipStream_t stream) {
+  const int32_t waves = multi_waves(a.q_tiles);
+  if (waves == 8) return launch_multi_t<HD, BS, 8>(a, stream);
+  if (waves == 4) return launch_multi_t<HD, BS, 4>(a, stream);
+  return launch_multi_t<HD, BS, 2>(a, stream);
 }
 
 }  // namespace
@@ -1586,13 +1903,13 @@ hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream) {
 
 hipError_t launch_multi(const DecodeArgs &a, hipStream_t stream) {
   if (a.head_dim == 128) {
-    if (a.block_size == 8) return launch_multi_t<128, 8>(a, stream);
-    if (a.block_size == 16) return launch_multi_t<128, 16>(a, stream);
-    return launch_multi_t<128, 32>(a, stream);
+    if (a.block_size == 8) return launch_multi_shape<128, 8>(a, stream);
+    if (a.block_size == 16) return launch_multi_shape<128, 16>(a, stream);
+    return launch_multi_shape<128, 32>(a, stream);
   }
-  if (a.block_size == 8) return launch_multi_t<64, 8>(a, stream);
-  if (a.block_size == 16) return launch_multi_t<64, 16>(a, stream);
-  return launch_multi_t<64, 32>(a, stream);
+  if (a.block_size == 8) return launch_multi_shape<64, 8>(a, stream);
+  if (a.block_size == 16) return launch_multi_shape<64, 16>(a, stream);
+  return launch_multi_shape<64, 32>(a, stream);
 }
 
 }  // namespace pkv

@@ -25,9 +25,20 @@ struct DecodeArgs {
   int64_t num_blocks;
   int32_t dtype, out_dtype;
   float scale;
-  // multi-query read: queries per row, query tiles per row, queries per tile
-  int32_t query_len, q_tiles, q_per_tile;
+  // multi-query read: queries per row, 32-column tiles per (row, kv head),
+  // queries per tile, query blocks (one workgroup each) per (row, kv head)
+  int32_t query_len, q_tiles, q_per_tile, q_blocks;
 };
+
+// Multi-query read: a workgroup of multi_waves(tiles) waves, one 32-column
+// score tile each, covers that many tiles of one (row, kv head) and shares
+// every staged K/V group among them.
+__host__ __device__ inline int32_t multi_waves(int32_t tiles) { return tiles > 4 ? 8 : (tiles > 2 ? 4 : 2); }
+// LDS ring depth of the multi-query read, in 32-position groups: eight for
+// a workgroup that has its compute unit to itself (eight waves), four where
+// two workgroups share one.
+__host__ __device__ constexpr int multi_ring(int waves) { return waves >= 8 ? 8 : 4; }
+constexpr int kMultiMaxPartition = 1024;   // positions per multi-query partition, at most
 
 // Workspace of the split-context read, in floats: running max m and sum l
 // per (row, query head, partition), then the fp32 partial output rows.

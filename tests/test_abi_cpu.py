@@ -248,11 +248,16 @@ def test_multi_query_refusals(lib):
 
 def test_multi_query_workspace(lib):
     ws = lambda d, q: lib.pkv_paged_attention_multi_workspace_size(ctypes.byref(d), q)
-    # 64 rows x 8 kv heads x one 4-query tile = 512 tiles: two waves per tile
-    # wanted gives 2048 positions, capped at 512, so a 4096-position table
-    # splits in 8: m, l and a 128-float acc per (row, query, head, partition)
+    # 64 rows x 8 kv heads x one query block (4 queries: one tile, a
+    # two-wave workgroup) = 512 blocks; 2048 workgroups wanted gives 1024
+    # positions, capped at 512, so a 4096-position table splits in 8: m, l
+    # and a 128-float acc per (row, query, head, partition)
     d = desc()
     slots = 64 * 4 * 32 * 8
     assert ws(d, 4) == (((2 * slots + 3) & ~3) + slots * 128) * 4
-    assert ws(desc(partition_tokens=4096), 4) == 0   # one partition: written directly
+    # a caller's partition is capped at 1024 positions: 4 partitions
+    slots4 = 64 * 4 * 32 * 4
+    assert ws(desc(partition_tokens=1024), 4) == (((2 * slots4 + 3) & ~3) + slots4 * 128) * 4
+    assert ws(desc(partition_tokens=4096), 4) == ws(desc(partition_tokens=1024), 4)
+    assert ws(desc(max_blocks_per_row=64, partition_tokens=1024), 4) == 0   # one partition: written directly
     assert ws(desc(dtype=0, out_dtype=0), 4) == 0    # refused descriptors need nothing

@@ -456,6 +456,11 @@ def multi_oracle(b, q):
     (32, 8, 128, 16, 40, 300, 16, 0), (32, 8, 128, 8, 60, 400, 33, 64), (32, 8, 128, 32, 1, 400, 8, 32),
     (8, 1, 64, 16, 1, 200, 6, 0), (8, 1, 64, 8, 100, 500, 3, 96), (16, 16, 64, 32, 1, 150, 2, 0),
     (24, 2, 128, 16, 1, 260, 7, 64),
+    # query blocks of several waves (32-column tiles, one per wave): 13 tiles
+    # (two blocks of 8 waves), 3 tiles (4 waves), 2 tiles (2 waves, partition
+    # capped at 1024), one query per head (G = 1, 10 tiles), G = 8 (10 tiles)
+    (32, 8, 128, 16, 100, 700, 100, 0), (32, 8, 128, 8, 80, 600, 20, 1024), (32, 8, 128, 32, 30, 500, 12, 4096),
+    (16, 16, 64, 16, 300, 900, 300, 256), (8, 1, 64, 8, 50, 700, 40, 0),
 ])
 def test_multi_query_read_matches_oracle(H, KV, hd, bs, lo, hi, qlen, part):
     note("multi H=%d KV=%d hd=%d bs=%d q=%d part=%d" % (H, KV, hd, bs, qlen, part))
