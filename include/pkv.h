@@ -174,7 +174,8 @@ size_t pkv_paged_attention_workspace_size(const pkv_attn_desc *d);
  *
  *   d             as for pkv_paged_attention; dtype must be PKV_BF16 and
  *                 head_dim 64 or 128 (else PKV_ERR_DTYPE / PKV_ERR_HEAD_DIM);
- *                 partition_tokens is rounded up to a multiple of 32
+ *                 partition_tokens is rounded up to a multiple of 32 and
+ *                 capped at 4096 (0: chosen from the shapes)
  *   query_len     1 .. 65535
  *   q, out        device [rows, query_len, n_heads, head_dim]
  *   workspace     >= pkv_paged_attention_multi_workspace_size(d, query_len)

@@ -7,6 +7,8 @@
 // would be a device sync on every call.
 #include <limits.h>
 
+#include <algorithm>
+
 #include "pkv.h"
 #include "pkv_internal.h"
 
@@ -108,9 +110,13 @@ int plan_decode(const pkv_attn_desc *d, Plan *pl) {
 
 // Multi-query read: bf16, head_dim 64/128.  Partitions are whole 32-position
 // groups, at most kMultiMaxPartition positions: the caller's partition_tokens
-// rounded up to a group (and capped), else a default that gives about
-// kTargetMultiWaves waves over all workgroups.
-constexpr int64_t kTargetMultiWaves = 4096;
+// rounded up to a group (and capped), else the power of two (256 .. 2048)
+// nearest below the one that makes the largest possible grid about one
+// workgroup per slot of the GPU (kComputeUnits compute units times the
+// workgroups of this shape one unit holds).  Larger partitions mean fewer
+// start-ups and partial results; measured on the 8B shape, one slot per
+// workgroup beat both finer and coarser cuts.
+constexpr int64_t kComputeUnits = 256;
 struct MultiPlan {
   int32_t q_tiles, q_per_tile, q_blocks;
 };
@@ -131,9 +137,10 @@ int plan_multi(const pkv_attn_desc *d, int32_t query_len, Plan *pl, MultiPlan *m
     part = (d->partition_tokens + g32 - 1) / g32 * g32;
   } else {
     const int64_t blocks = (int64_t)mp->q_blocks * d->n_kv_heads * (d->rows > 0 ? d->rows : 1);
-    const int64_t want_wgs = (kTargetMultiWaves / waves + blocks - 1) / blocks;
-    part = ((cap + want_wgs - 1) / want_wgs + g32 - 1) / g32 * g32;
-    if (part > kDefaultPartition) part = kDefaultPartition;
+    const int64_t per_cu = std::max<int64_t>(1, (d->head_dim == 128 ? 4 : 8) / waves);  // registers, LDS
+    const int64_t want = (int64_t)cap * blocks / (kComputeUnits * per_cu);
+    part = 256;
+    while (part < 2048 && part * 2 <= want) part *= 2;
   }
   if (part > pkv::kMultiMaxPartition) part = pkv::kMultiMaxPartition;
   if (part < g32) part = g32;

@@ -1824,34 +1824,63 @@ decode_multi(DecodeArgs a) {
   }
 }
 
-// Combine the partitions of one (row, query, head) of the multi-query read:
-// M = max_k m_k over partitions that saw something; out = sum_k acc_k 2^(m_k - M)
-// / sum_k l_k 2^(m_k - M), or zeros when no partition saw a position.
-__global__ __launch_bounds__(128) void decode_multi_merge(DecodeArgs a) {
+// Combine the partitions of the multi-query read, 32 lanes per (row, query,
+// head): lane j reads partition j's (m, l); M = max m_j over partitions that
+// saw something, w_j = 2^(m_j - M) (0 for those that did not), L = sum l_j
+// w_j, and each lane sums w_j acc_j over its four hd values, the loads of
+// several partitions in flight at once.  out = O / L, or zeros when nothing
+// was visible.  kMultiMergeTuples tuples per 256-thread workgroup.
+constexpr int kMultiMergeTuples = 8;
+__global__ __launch_bounds__(256) void decode_multi_merge(DecodeArgs a) {
   const int Q = a.query_len, HD = a.head_dim;
-  const size_t vh = blockIdx.x;  // ((row * Q + query) * n_heads + head)
+  const int sub = threadIdx.x & 31;
+  const size_t vh = (size_t)blockIdx.x * kMultiMergeTuples + (threadIdx.x >> 5);  // (row * Q + query) * n_heads + head
+  if (vh >= (size_t)a.rows * Q * a.n_heads) return;  // a whole 32-lane half
   const int r = (int)(vh / ((size_t)Q * a.n_heads));
   const int cap = a.max_blocks_per_row * a.block_size;
   int n = a.context_lens[r];
   n = n < 0 ? 0 : (n > cap ? cap : n);
   const int nparts = n > 0 ? (n + a.partition_tokens - 1) / a.partition_tokens : 1;
-  if (nparts <= 1) return;
+  if (nparts <= 1) return;  // written directly by decode_multi
   const WsLayout W = ws_layout(a.rows * Q, a.n_heads, a.max_parts, HD);
   const size_t s0 = vh * a.max_parts;
   float M = -INFINITY;
-  for (int k = 0; k < nparts; ++k) M = fmaxf(M, a.ws[W.m_off + s0 + k]);
-  for (int d = threadIdx.x; d < HD; d += blockDim.x) {
-    float L = 0.f, O = 0.f;
-    if (M != -INFINITY) {
-      for (int k = 0; k < nparts; ++k) {
-        const float mk = a.ws[W.m_off + s0 + k];
-        if (mk == -INFINITY) continue;
-        const float w = exp2_fast(mk - M);
-        L = fmaf(a.ws[W.l_off + s0 + k], w, L);
-        O = fmaf(a.ws[W.acc_off + (s0 + k) * HD + d], w, O);
-      }
+  for (int j0 = 0; j0 < nparts; j0 += 32)
+    if (j0 + sub < nparts) M = fmaxf(M, a.ws[W.m_off + s0 + j0 + sub]);
+#pragma unroll
+  for (int x = 16; x >= 1; x >>= 1) M = fmaxf(M, __shfl_xor(M, x, 32));
+  const int d = 4 * sub;  // this lane's hd values d .. d + 3
+  float L = 0.f;
+  f32x4_t O = {0.f, 0.f, 0.f, 0.f};
+  for (int j0 = 0; j0 < nparts; j0 += 32) {
+    float w = 0.f;
+    if (j0 + sub < nparts && M != -INFINITY) {
+      const float mj = a.ws[W.m_off + s0 + j0 + sub];
+      w = mj == -INFINITY ? 0.f : exp2_fast(mj - M);
+      L = fmaf(a.ws[W.l_off + s0 + j0 + sub], w, L);
     }
-    store_out(a.out, a.out_dtype, vh * HD + d, L > 0.f ? O / L : 0.f);
+    const int cnt = min(32, nparts - j0);
+    const float *acc = a.ws + W.acc_off + (s0 + j0) * HD + d;
+    int t = 0;
+    for (; t + 4 <= cnt; t += 4) {  // four partitions' loads in flight
+      f32x4_t x[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u)
+        x[u] = d < HD ? *reinterpret_cast<const f32x4_t *>(acc + (size_t)(t + u) * HD) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) O += __shfl(w, t + u, 32) * x[u];
+    }
+    for (; t < cnt; ++t) {
+      const f32x4_t x = d < HD ? *reinterpret_cast<const f32x4_t *>(acc + (size_t)t * HD) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      O += __shfl(w, t, 32) * x;
+    }
+  }
+#pragma unroll
+  for (int x = 16; x >= 1; x >>= 1) L += __shfl_xor(L, x, 32);
+  if (d < HD) {
+    const float inv = L > 0.f ? 1.f / L : 0.f;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) store_out(a.out, a.out_dtype, vh * HD + d + e, L > 0.f ? O[e] * inv : 0.f);
   }
 }
 
@@ -1861,8 +1890,9 @@ hipError_t launch_multi_t(const DecodeArgs &a, hipStream_t stream) {
   hipLaunchKernelGGL((decode_multi<HD, BS, NW>), dim3((unsigned)units), dim3(NW * kWave), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
-  hipLaunchKernelGGL(decode_multi_merge, dim3((unsigned)((size_t)a.rows * a.query_len * a.n_heads)), dim3(128), 0,
-                     stream, a);
+  const size_t tuples = (size_t)a.rows * a.query_len * a.n_heads;
+  hipLaunchKernelGGL(decode_multi_merge, dim3((unsigned)((tuples + kMultiMergeTuples - 1) / kMultiMergeTuples)),
+                     dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

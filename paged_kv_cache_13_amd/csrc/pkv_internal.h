@@ -38,7 +38,7 @@ __host__ __device__ inline int32_t multi_waves(int32_t tiles) { return tiles > 4
 // a workgroup that has its compute unit to itself (eight waves), four where
 // two workgroups share one.
 __host__ __device__ constexpr int multi_ring(int waves) { return waves >= 8 ? 8 : 4; }
-constexpr int kMultiMaxPartition = 1024;   // positions per multi-query partition, at most
+constexpr int kMultiMaxPartition = 4096;   // positions per multi-query partition, at most
 
 // Workspace of the split-context read, in floats: running max m and sum l
 // per (row, query head, partition), then the fp32 partial output rows.
