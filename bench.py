@@ -31,7 +31,7 @@ HBM_PEAK_GBS = 8000.0
 # a plain copy of known size (profiles/decode_stream_<workload>_hbm_counters.md),
 # valid only for the kernel sources they were taken on.
 PROFILED_TRAFFIC = {
-    "llama3_8b_layer": {"src": "6a8e55044bcbbeed", "read_bytes": 577796395},
+    "llama3_8b_layer": {"src": "183b89270972c6cd", "read_bytes": 577694098},
 }
 KERNEL_SOURCES = ("decode.hip", "pkv_internal.h", "abi.hip")
 
@@ -64,6 +64,9 @@ def parse():
                     help="target CPU time of the oracle baseline (0 disables it)")
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the other workloads (small fp32 reads, skewed batch, decode runs)")
+    ap.add_argument("--prefill-chunk-only", action="store_true",
+                    help="only time the multi-query read of a 64-query chunk over 16 rows of the 8B "
+                         "layer (the prefill_chunk entry of other_workloads) and print it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (a kernel of "
                          "known traffic, to scale HBM counters by) and exit")
@@ -312,6 +315,10 @@ def main():
                           "copy_calibration_bytes_written": dst.numel() * 4, "calls": 5}))
         return
     pkv.load_library()
+    if args.prefill_chunk_only:
+        stream = torch.cuda.current_stream()
+        print(json.dumps({"prefill_chunk": prefill_chunk(dev, stream)}), flush=True)
+        return
     cfg = synth.CONFIGS[args.workload]
     batch = synth.make_batch(cfg, device=dev)
     bs = cfg.block_size
