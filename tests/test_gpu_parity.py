@@ -476,6 +476,27 @@ def test_multi_query_read_matches_oracle(H, KV, hd, bs, lo, hi, qlen, part):
     assert_close(got32.cpu(), ref, what="multi fp32 out", **TOL[torch.float32])
 
 
+@pytest.mark.parametrize("bs,qlen", [(8, 20), (32, 70)])
+def test_multi_query_ignores_poisoned_slots_bitwise(bs, qlen):
+    # unused table entries point at a NaN block and slots past each row's end
+    # hold NaN (P6): the output must not change, bit for bit
+    cfg = synth.DecodeConfig("multi", "bf16", rows=5, n_heads=32, n_kv_heads=8, head_dim=128, block_size=bs,
+                             ctx=("uniform", 1, 900), pool=("factor", 1.5), max_ctx=900, seed=61)
+    clean = synth.make_batch(cfg, device=DEV, poison=False)
+    dirty = synth.make_batch(cfg, device=DEV, poison=True)
+    assert torch.isnan(dirty.k_pool.float()).any() and torch.isnan(dirty.v_pool.float()).any()
+    g = torch.Generator(device=DEV).manual_seed(62)
+    q = torch.randn(5, qlen, 32, 128, generator=g, device=DEV).to(torch.bfloat16)
+    outs = []
+    for b in (clean, dirty):
+        outs.append(pkv.paged_attention_multi(q, b.k_pool, b.v_pool, b.block_table, b.context_lens, b.scale,
+                                              out=torch.empty(q.shape, dtype=torch.float32, device=DEV),
+                                              partition_tokens=64))
+    torch.cuda.synchronize()
+    assert torch.isfinite(outs[1]).all()
+    assert torch.equal(outs[0], outs[1])
+
+
 def test_multi_query_rows_shorter_than_the_chunk_read_zeros():
     b, q = multi_case(6, 32, 8, 128, 16, 1, 6, 8, seed=41)
     got = pkv.paged_attention_multi(q, b.k_pool, b.v_pool, b.block_table, b.context_lens, b.scale)
