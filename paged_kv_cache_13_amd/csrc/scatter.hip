@@ -50,12 +50,23 @@ __global__ __launch_bounds__(kThreads) void scatter_kv(const uint4 *__restrict__
 }
 
 // Many tokens (a prompt): one workgroup per tile of kTileTokens consecutive
-// tokens.  K is copied as above.  V goes through LDS: the tile's rows are
-// read whole, then written out transposed, lane i carrying token i of the
-// tile for one (kv head, dimension) -- tokens that fill consecutive offsets
-// of one block (the prompt case) land as one contiguous run per element.
+// tokens.  K is copied as above.  V, one kv head at a time: the tile's
+// [tokens][head_dim] rows are loaded whole (16-byte chunks) and written into
+// LDS transposed, [head_dim][tokens] (bf16: a token pair per 32-bit word,
+// packed with a byte permute).  Then each run of 8 tokens of one dimension
+// is stored with 16-byte stores wherever those tokens fill 8 consecutive
+// offsets of one block starting at a multiple of 8 -- what a prompt's rows
+// do -- and element by element otherwise (padding, out-of-pool slots and
+// scattered tokens included).
 constexpr int kTileTokens = 32;
-constexpr int kTileLdsBytes = 64 * 1024;
+
+template <typename E>
+struct VTile {
+  // 32-bit words per LDS row of one dimension: bf16 16 (token pairs), fp32
+  // 32, plus 4 of padding (rows stay 16-byte aligned, and consecutive rows
+  // start on other banks)
+  static constexpr int kPitch = (sizeof(E) == 2 ? kTileTokens / 2 : kTileTokens) + 4;
+};
 
 template <typename E>
 __global__ __launch_bounds__(kThreads) void scatter_kv_tiled(const uint4 *__restrict__ k,
@@ -65,10 +76,11 @@ __global__ __launch_bounds__(kThreads) void scatter_kv_tiled(const uint4 *__rest
                                                              E *__restrict__ v_pool, int64_t num_tokens,
                                                              int64_t num_slots, int32_t log2_bs,
                                                              int32_t n_kv_heads, int32_t head_dim) {
-  constexpr int EC = kTileLdsBytes / kTileTokens / (int)sizeof(E) - 16;  // elements per chunk of a row
-  constexpr int ROW = EC + 16 / (int)sizeof(E) + 1;  // padded LDS row: consecutive tokens on other banks
-  __shared__ E s_v[kTileTokens * ROW];
+  constexpr bool kBF16 = sizeof(E) == 2;
+  constexpr int PITCH = VTile<E>::kPitch;
+  __shared__ uint32_t s_t[128 * PITCH];  // head_dim <= 128
   __shared__ int64_t s_slot[kTileTokens];
+  __shared__ int s_run[kTileTokens / 8];
   const int64_t t0 = (int64_t)blockIdx.x * kTileTokens;
   const int nt = (int)min<int64_t>(kTileTokens, num_tokens - t0);
   if (threadIdx.x < kTileTokens) {
@@ -76,6 +88,13 @@ __global__ __launch_bounds__(kThreads) void scatter_kv_tiled(const uint4 *__rest
     s_slot[threadIdx.x] = (s < 0 || s >= num_slots) ? -1 : s;  // padding or out of the pool: skipped
   }
   __syncthreads();
+  if (threadIdx.x < kTileTokens / 8) {  // tokens 8g .. 8g+7 fill offsets 8m .. 8m+7 of one block
+    const int g = threadIdx.x;
+    const int64_t s0 = s_slot[8 * g];
+    bool run = s0 >= 0 && (s0 & 7) == 0;
+    for (int j = 1; j < 8; ++j) run = run && s_slot[8 * g + j] == s0 + j;
+    s_run[g] = run;
+  }
   const int row_chunks = head_dim * (int)sizeof(E) / 16;
   const int k_chunks = n_kv_heads * row_chunks;
   for (int f = threadIdx.x; f < nt * k_chunks; f += kThreads) {
@@ -88,25 +107,64 @@ __global__ __launch_bounds__(kThreads) void scatter_kv_tiled(const uint4 *__rest
     k_pool[dst] = k[(size_t)(t0 + i) * k_chunks + c];
   }
   const int v_elems = n_kv_heads * head_dim;
-  constexpr int VEC = 16 / (int)sizeof(E);
-  for (int e0 = 0; e0 < v_elems; e0 += EC) {
-    const int ec = min(EC, v_elems - e0);  // a multiple of VEC: head_dim is
-    __syncthreads();                        // the LDS tile is free again
-    for (int f = threadIdx.x; f < nt * (ec / VEC); f += kThreads) {
-      const int i = f / (ec / VEC), c = f - i * (ec / VEC);
-      const uint4 x = reinterpret_cast<const uint4 *>(v + (size_t)(t0 + i) * v_elems + e0)[c];
-      const E *xe = reinterpret_cast<const E *>(&x);
+  const int bmask = (1 << log2_bs) - 1;
+  for (int h = 0; h < n_kv_heads; ++h) {
+    __syncthreads();  // the LDS tile is free again (and s_run is written)
+    if constexpr (kBF16) {
+      // token pair p, dimensions 8c .. 8c+7
+      const int items = (kTileTokens / 2) * (head_dim / 8);
+      for (int f = threadIdx.x; f < items; f += kThreads) {
+        const int p = f % (kTileTokens / 2), c = f / (kTileTokens / 2);
+        const int i0 = 2 * p, i1 = 2 * p + 1;
+        const size_t col = (size_t)h * head_dim + 8 * c;
+        const uint4 x0 = i0 < nt ? *reinterpret_cast<const uint4 *>(v + (size_t)(t0 + i0) * v_elems + col)
+                                 : make_uint4(0, 0, 0, 0);
+        const uint4 x1 = i1 < nt ? *reinterpret_cast<const uint4 *>(v + (size_t)(t0 + i1) * v_elems + col)
+                                 : make_uint4(0, 0, 0, 0);
+        const uint32_t a0[4] = {x0.x, x0.y, x0.z, x0.w}, a1[4] = {x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-      for (int u = 0; u < VEC; ++u) s_v[i * ROW + c * VEC + u] = xe[u];
+        for (int w = 0; w < 4; ++w) {  // dimensions 8c + 2w (low halves) and 8c + 2w + 1 (high halves)
+          s_t[(8 * c + 2 * w) * PITCH + p] = __builtin_amdgcn_perm(a1[w], a0[w], 0x05040100u);
+          s_t[(8 * c + 2 * w + 1) * PITCH + p] = __builtin_amdgcn_perm(a1[w], a0[w], 0x07060302u);
+        }
+      }
+    } else {
+      // token i, dimensions 4c .. 4c+3
+      const int items = kTileTokens * (head_dim / 4);
+      for (int f = threadIdx.x; f < items; f += kThreads) {
+        const int i = f % kTileTokens, c = f / kTileTokens;
+        const uint4 x = i < nt ? *reinterpret_cast<const uint4 *>(v + (size_t)(t0 + i) * v_elems + (size_t)h * head_dim +
+                                                                  4 * c)
+                               : make_uint4(0, 0, 0, 0);
+        s_t[(4 * c) * PITCH + i] = x.x;
+        s_t[(4 * c + 1) * PITCH + i] = x.y;
+        s_t[(4 * c + 2) * PITCH + i] = x.z;
+        s_t[(4 * c + 3) * PITCH + i] = x.w;
+      }
     }
     __syncthreads();
-    for (int f = threadIdx.x; f < kTileTokens * ec; f += kThreads) {
-      const int i = f % kTileTokens, e = f / kTileTokens;
-      if (i >= nt) continue;
-      const int64_t s = s_slot[i];
-      if (s < 0) continue;
-      const size_t dst = (((size_t)(s >> log2_bs) * v_elems + e0 + e) << log2_bs) + (s & ((1 << log2_bs) - 1));
-      v_pool[dst] = s_v[i * ROW + e];
+    // dimension d, tokens 8g .. 8g+7 (g fastest: a row's runs side by side)
+    for (int f = threadIdx.x; f < head_dim * (kTileTokens / 8); f += kThreads) {
+      const int g = f & 3, d = f >> 2;
+      const uint32_t *row = s_t + d * PITCH;
+      if (s_run[g]) {
+        const int64_t s0 = s_slot[8 * g];
+        E *dst = v_pool + ((((size_t)(s0 >> log2_bs) * n_kv_heads + h) * head_dim + d) << log2_bs) + (s0 & bmask);
+        if constexpr (kBF16) {
+          *reinterpret_cast<uint4 *>(dst) = *reinterpret_cast<const uint4 *>(row + 4 * g);
+        } else {
+          reinterpret_cast<uint4 *>(dst)[0] = *reinterpret_cast<const uint4 *>(row + 8 * g);
+          reinterpret_cast<uint4 *>(dst)[1] = *reinterpret_cast<const uint4 *>(row + 8 * g + 4);
+        }
+      } else {
+        for (int j = 0; j < 8; ++j) {
+          const int i = 8 * g + j;
+          const int64_t s = s_slot[i];
+          if (s < 0) continue;
+          const E e = kBF16 ? (E)(row[i >> 1] >> (16 * (i & 1))) : (E)row[i];
+          v_pool[((((size_t)(s >> log2_bs) * n_kv_heads + h) * head_dim + d) << log2_bs) + (s & bmask)] = e;
+        }
+      }
     }
   }
 }
