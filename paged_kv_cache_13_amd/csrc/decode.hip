@@ -1621,15 +1621,24 @@ __device__ __forceinline__ void multi_pair(MultiState<HD> &S, const uint4 *c0, c
   float raw0[16], raw1[16];
   multi_raw<HD>(raw0, sc0, S, gb0, h, true);
   multi_raw<HD>(raw1, sc1, S, gb1, h, two);
-  // c > 0: the column max of the raw dot products, times c, is the max of
-  // its scores
-  float mx = fmaxf(raw0[0], raw1[0]);
+  // Does any score of this lane exceed its column's reference by more than
+  // kLazyRescale?  With c > 0, raw > (m + kLazyRescale) / c is that test (up
+  // to rounding at the threshold, which only lets a weight reach 2^8 times a
+  // rounding error); it needs no data from other lanes.  The threshold is
+  // -inf while the column has seen nothing.
+  const float thr = (S.m + kLazyRescale) / cscale;
+  bool over = false;
 #pragma unroll
-  for (int j = 1; j < 16; ++j) mx = fmaxf(mx, fmaxf(raw0[j], raw1[j]));
-  mx = fmaxf(mx, __shfl_xor(mx, 32));
-  const float mxs = mx * cscale;  // -inf when the column sees nothing here
-  const bool up = mxs > S.m + kLazyRescale;
-  if (__any(up)) {  // move the reference max of the columns that outgrew it
+  for (int j = 0; j < 16; ++j) over |= (raw0[j] > thr) | (raw1[j] > thr);
+  if (__any(over)) {  // rare after a partition's first pair
+    // c > 0: the column max of the raw dot products, times c, is the max of
+    // its scores; move the reference of the columns that outgrew it
+    float mx = fmaxf(raw0[0], raw1[0]);
+#pragma unroll
+    for (int j = 1; j < 16; ++j) mx = fmaxf(mx, fmaxf(raw0[j], raw1[j]));
+    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    const float mxs = mx * cscale;  // -inf when the column sees nothing here
+    const bool up = mxs > S.m + kLazyRescale;
     const float alpha = up ? exp2_fast(S.m - mxs) : 1.f;  // 0 from -inf
     S.m = up ? mxs : S.m;
     S.l *= alpha;
