@@ -461,6 +461,9 @@ def multi_oracle(b, q):
     # capped at 1024), one query per head (G = 1, 10 tiles), G = 8 (10 tiles)
     (32, 8, 128, 16, 100, 700, 100, 0), (32, 8, 128, 8, 80, 600, 20, 1024), (32, 8, 128, 32, 30, 500, 12, 4096),
     (16, 16, 64, 16, 300, 900, 300, 256), (8, 1, 64, 8, 50, 700, 40, 0),
+    # the 8-wave block (8-group ring) with 8-position blocks (four per
+    # group) and 32-position blocks, default partitions
+    (32, 8, 128, 8, 200, 900, 64, 0), (32, 8, 128, 32, 200, 900, 64, 0),
 ])
 def test_multi_query_read_matches_oracle(H, KV, hd, bs, lo, hi, qlen, part):
     note("multi H=%d KV=%d hd=%d bs=%d q=%d part=%d" % (H, KV, hd, bs, qlen, part))
