@@ -175,7 +175,12 @@ size_t pkv_paged_attention_workspace_size(const pkv_attn_desc *d);
  *   d             as for pkv_paged_attention; dtype must be PKV_BF16 and
  *                 head_dim 64 or 128 (else PKV_ERR_DTYPE / PKV_ERR_HEAD_DIM);
  *                 partition_tokens is rounded up to a multiple of 32 and
- *                 capped at 4096 (0: chosen from the shapes)
+ *                 capped at 4096 (0: chosen from the shapes).  A chunk with
+ *                 query_len * (n_heads / n_kv_heads) <= 16 over a table of
+ *                 at least 32 * 1024 groups of 32 positions (rows x kv heads
+ *                 x table width) runs on pkv_paged_attention's stream
+ *                 decomposition instead, where partition_tokens is the
+ *                 minimum slice length as there.
  *   query_len     1 .. 65535
  *   q, out        device [rows, query_len, n_heads, head_dim]
  *   workspace     >= pkv_paged_attention_multi_workspace_size(d, query_len)

@@ -117,8 +117,10 @@ int plan_decode(const pkv_attn_desc *d, Plan *pl) {
 // start-ups and partial results; measured on the 8B shape, one slot per
 // workgroup beat both finer and coarser cuts.
 constexpr int64_t kComputeUnits = 256;
+constexpr int64_t kStreamMultiGroups = 32;
 struct MultiPlan {
   int32_t q_tiles, q_per_tile, q_blocks;
+  int32_t stream;  // 1: query_len * group <= 16 columns on the stream path
 };
 int plan_multi(const pkv_attn_desc *d, int32_t query_len, Plan *pl, MultiPlan *mp) {
   const int st = plan_decode(d, pl);
@@ -126,6 +128,23 @@ int plan_multi(const pkv_attn_desc *d, int32_t query_len, Plan *pl, MultiPlan *m
   if (d->dtype != PKV_BF16) return PKV_ERR_DTYPE;
   if (d->head_dim != 64 && d->head_dim != 128) return PKV_ERR_HEAD_DIM;
   if (query_len < 1 || query_len > 65535) return PKV_ERR_SHAPE;
+  // A chunk whose (query, head) pairs fit the 16 columns of the one-query
+  // read's score tile runs on that read's stream decomposition -- the same
+  // bytes, in columns the one-query read leaves empty -- when the table can
+  // hold at least kStreamMultiGroups groups per persistent wave.  Below
+  // that the stream is latency-bound and the workgroup kernel is faster
+  // (8B-shaped layer, 4 queries: 16 rows 54 vs 60 us, 64 rows 179 vs 129 us).
+  const int64_t cap_groups = ((int64_t)d->max_blocks_per_row * d->block_size + pkv::kGroupPositions - 1) /
+                             pkv::kGroupPositions;
+  mp->stream = pl->stream && (int64_t)query_len * pl->group <= 16 &&
+               (int64_t)d->rows * d->n_kv_heads * cap_groups >= kStreamMultiGroups * pkv::kStreamWaves;
+  if (mp->stream) {
+    mp->q_tiles = mp->q_per_tile = mp->q_blocks = 0;
+    pl->ws_bytes = d->rows > 0 ? pkv::stream_layout(d->rows, d->n_kv_heads, query_len * pl->group, d->head_dim,
+                                                    pl->max_parts).total * sizeof(int32_t)
+                               : 0;
+    return PKV_OK;
+  }
   const int32_t cap = d->max_blocks_per_row * d->block_size;
   mp->q_per_tile = 32 / pl->group;  // group <= 16
   mp->q_tiles = (query_len + mp->q_per_tile - 1) / mp->q_per_tile;
@@ -184,7 +203,7 @@ int launch_attention(const pkv_attn_desc *d, const Plan &pl, const void *q, cons
                      const void *v_pool, const int32_t *block_table, const int32_t *context_lens,
                      float scale, void *out, void *workspace, hipStream_t stream) {
   if (d->rows == 0) return PKV_OK;
-  pkv::DecodeArgs a;
+  pkv::DecodeArgs a = {};
   a.q = q;
   a.k_pool = k_pool;
   a.v_pool = v_pool;
@@ -209,6 +228,8 @@ int launch_attention(const pkv_attn_desc *d, const Plan &pl, const void *q, cons
   a.dtype = d->dtype;
   a.out_dtype = d->out_dtype;
   a.scale = scale;
+  a.query_len = 1;
+  a.cols = pl.group;
   return pkv::launch_decode(a, stream) == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
@@ -316,6 +337,36 @@ int pkv_paged_attention_multi(const pkv_attn_desc *d, int32_t query_len, const v
     if (!aligned(workspace, 16)) return PKV_ERR_ALIGN;
   }
   if (d->rows == 0) return PKV_OK;
+  if (mp.stream) {  // the one-query read's kernels, query_len * group columns
+    pkv::DecodeArgs a = {};
+    a.q = q;
+    a.k_pool = k_pool;
+    a.v_pool = v_pool;
+    a.block_table = block_table;
+    a.context_lens = context_lens;
+    a.out = out;
+    a.ws = pl.ws_bytes ? static_cast<float *>(workspace) : nullptr;
+    a.rows = d->rows;
+    a.n_heads = d->n_heads;
+    a.n_kv_heads = d->n_kv_heads;
+    a.group = pl.group;
+    a.head_dim = d->head_dim;
+    a.block_size = d->block_size;
+    a.log2_bs = pl.log2_bs;
+    a.max_blocks_per_row = d->max_blocks_per_row;
+    a.partition_tokens = pl.partition;
+    a.max_parts = pl.max_parts;
+    a.stream = 1;
+    a.cg_min = pl.cg_min;
+    a.inplan = d->rows <= pkv::kWindowRows;
+    a.num_blocks = d->num_blocks;
+    a.dtype = d->dtype;
+    a.out_dtype = d->out_dtype;
+    a.scale = scale;
+    a.query_len = query_len;
+    a.cols = query_len * pl.group;
+    return pkv::launch_decode(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
+  }
   pkv::DecodeArgs a = {};
   a.q = q;
   a.k_pool = k_pool;

@@ -727,7 +727,7 @@ __global__ __launch_bounds__(1024) void decode_plan(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int rows = a.rows;
   const int cap = a.max_blocks_per_row * a.block_size;
-  const StreamLayout L = stream_layout(rows, a.n_kv_heads, a.group, a.head_dim, a.max_parts);
+  const StreamLayout L = stream_layout(rows, a.n_kv_heads, a.cols, a.head_dim, a.max_parts);
   int32_t *wsi = reinterpret_cast<int32_t *>(a.ws);
   const int per = (rows + 1023) / 1024;
   const int r0 = min(rows, tid * per), r1 = min(rows, r0 + per);
@@ -737,9 +737,9 @@ __global__ __launch_bounds__(1024) void decode_plan(DecodeArgs a) {
     n = n < 0 ? 0 : (n > cap ? cap : n);
     s_gpre[r] = local;
     local += (n + kGroupPositions - 1) / kGroupPositions;
-    if (n == 0) {  // an empty row reads zeros; no wave visits it
-      for (int idx = 0; idx < a.n_heads * a.head_dim; ++idx)
-        store_out(a.out, a.out_dtype, (size_t)r * a.n_heads * a.head_dim + idx, 0.f);
+    if (n == 0) {  // an empty row reads zeros (all its queries); no wave visits it
+      const size_t per_row = (size_t)a.query_len * a.n_heads * a.head_dim;
+      for (size_t idx = 0; idx < per_row; ++idx) store_out(a.out, a.out_dtype, (size_t)r * per_row + idx, 0.f);
     }
   }
   s_sum[tid] = local;
@@ -969,10 +969,14 @@ __device__ __forceinline__ void group_scores(const bf16x8_t (&k)[2][HD / 32], co
     for (int i = 0; i < KS; ++i) sacc[tt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(k[tt][i], qb[i], sacc[tt], 0, 0, 0);
 }
 
-// Online-softmax update and P.V of one group from its scores.
+// Online-softmax update and P.V of one group from its scores.  `end` (per
+// lane): positions this lane's column sees; `row_end`: the row's length,
+// past which V is zeroed.  A column that has seen nothing yet keeps m = -inf
+// and takes 0 as its exponent reference, so all its weights are 0.
 template <int HD>
 __device__ __forceinline__ void group_softmax_pv(const f32x4_t (&sacc)[2], bf16x8_t (&v)[HD / 16], f32x4_t *acc,
-                                                 float &m, float &l, float c, int end, int gbase, int lg) {
+                                                 float &m, float &l, float c, int end, int row_end, int gbase,
+                                                 int lg) {
   constexpr int DT = HD / 16;
   const int tl = gbase + 8 * lg;
   float s[8];
@@ -985,10 +989,11 @@ __device__ __forceinline__ void group_softmax_pv(const f32x4_t (&sacc)[2], bf16x
   const float m_new = fmaxf(m, mx);
   const float alpha = (m == m_new) ? 1.f : exp2_fast(m - m_new);
   m = m_new;
+  const float mref = m_new == -INFINITY ? 0.f : m_new;
   float pv[8], psum = 0.f;
 #pragma unroll
   for (int e = 0; e < 8; ++e) {
-    pv[e] = exp2_fast(s[e] - m_new);
+    pv[e] = exp2_fast(s[e] - mref);
     psum += pv[e];
   }
   l = l * alpha + psum;
@@ -1007,8 +1012,8 @@ __device__ __forceinline__ void group_softmax_pv(const f32x4_t (&sacc)[2], bf16x
   }
   const bf16x8_t phi = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
   const bf16x8_t plo = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
-  if (gbase + 32 > end) {  // positions past the row end: zero their (possibly NaN) V
-    int nv = end - tl;
+  if (gbase + 32 > row_end) {  // positions past the row end: zero their (possibly NaN) V
+    int nv = row_end - tl;
     nv = nv < 0 ? 0 : (nv > 8 ? 8 : nv);
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) v[dt] = keep_first(v[dt], nv);
@@ -1020,11 +1025,17 @@ __device__ __forceinline__ void group_softmax_pv(const f32x4_t (&sacc)[2], bf16x
   }
 }
 
+// Output row of stream column `col` of (kv head, row): query col / group,
+// head kv head * group + col % group.
+__device__ __forceinline__ size_t stream_out_row(const DecodeArgs &a, int kvh, int r, int col) {
+  return ((size_t)r * a.query_len + col / a.group) * a.n_heads + kvh * a.group + col % a.group;
+}
+
 template <int HD>
 __device__ __forceinline__ void write_out_rows(const DecodeArgs &a, const Cursor &c, const f32x4_t *o,
                                                float inv, int lr, int lg) {
   constexpr int DT = HD / 16;
-  const size_t base = ((size_t)c.r * a.n_heads + c.kvh * a.group + lr) * HD + 4 * lg;
+  const size_t base = stream_out_row(a, c.kvh, c.r, lr) * HD + 4 * lg;
   if (a.out_dtype == kF32) {
     float *out = static_cast<float *>(a.out) + base;
 #pragma unroll
@@ -1048,18 +1059,18 @@ template <int HD>
 __device__ __forceinline__ void segment_end(const DecodeArgs &a, const StreamLayout &L, const Cursor &c,
                                             f32x4_t *acc, float &m, float &l, int lr, int lg) {
   constexpr int DT = HD / 16;
-  const int G = a.group;
+  const int C = a.cols;
   const float lt = sum_across_rows(l);
   if (c.nparts == 1) {
-    if (lr < G) write_out_rows<HD>(a, c, acc, 1.f / lt, lr, lg);
-  } else if (lr < G) {
+    if (lr < C) write_out_rows<HD>(a, c, acc, lt > 0.f ? 1.f / lt : 0.f, lr, lg);  // 0: a query before the history
+  } else if (lr < C) {
     const size_t pair = (size_t)c.kvh * a.rows + c.r;
     float *slot = a.ws + L.partials + (pair * a.max_parts + c.part) * L.slot_stride;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4_t *>(slot + lr * HD + 16 * dt + 4 * lg) = acc[dt];
     if (lg == 0) {
-      slot[G * HD + lr] = m;
-      slot[G * HD + G + lr] = lt;
+      slot[C * HD + lr] = m;
+      slot[C * HD + C + lr] = lt;
     }
   }
   m = -INFINITY;
@@ -1075,7 +1086,7 @@ __device__ __forceinline__ void segment_end(const DecodeArgs &a, const StreamLay
 // are read first (one independent load each), then the weighted sums.
 constexpr int kMergeMaxParts = 8;
 __global__ __launch_bounds__(256) void decode_stream_merge(DecodeArgs a) {
-  const StreamLayout L = stream_layout(a.rows, a.n_kv_heads, a.group, a.head_dim, a.max_parts);
+  const StreamLayout L = stream_layout(a.rows, a.n_kv_heads, a.cols, a.head_dim, a.max_parts);
   const int32_t *wsi = reinterpret_cast<const int32_t *>(a.ws);
   const int pair = blockIdx.x;
   const int kvh = pair / a.rows, r = pair - kvh * a.rows;
@@ -1120,9 +1131,9 @@ __global__ __launch_bounds__(256) void decode_stream_merge(DecodeArgs a) {
   const long long S = (long long)kvh * ngk + g0;
   const int nparts = (int)(slice_of(S + ng - 1, ng_all, waves) - slice_of(S, ng_all, waves) + 1);
   if (nparts <= 1) return;
-  const int G = a.group, HD = a.head_dim;
+  const int C = a.cols, HD = a.head_dim;
   const float *slots = a.ws + L.partials + (size_t)pair * a.max_parts * L.slot_stride;
-  for (int idx = threadIdx.x; idx < G * HD; idx += blockDim.x) {
+  for (int idx = threadIdx.x; idx < C * HD; idx += blockDim.x) {
     const int j = idx / HD, d = idx - j * HD;
     float M = -INFINITY, Lm = 0.f, O = 0.f;
     for (int k0 = 0; k0 < nparts; k0 += kMergeMaxParts) {
@@ -1132,8 +1143,8 @@ __global__ __launch_bounds__(256) void decode_stream_merge(DecodeArgs a) {
       for (int k = 0; k < kMergeMaxParts; ++k) {
         if (k < kn) {
           const float *sk = slots + (size_t)(k0 + k) * L.slot_stride;
-          mk[k] = sk[G * HD + j];
-          lk[k] = sk[G * HD + G + j];
+          mk[k] = sk[C * HD + j];
+          lk[k] = sk[C * HD + C + j];
           ak[k] = sk[j * HD + d];
         }
       }
@@ -1146,7 +1157,7 @@ __global__ __launch_bounds__(256) void decode_stream_merge(DecodeArgs a) {
       O *= a0;
 #pragma unroll
       for (int k = 0; k < kMergeMaxParts; ++k) {
-        if (k < kn) {
+        if (k < kn && mk[k] != -INFINITY) {  // a slice that saw nothing of this column adds nothing
           const float wk = exp2_fast(mk[k] - mn);
           Lm = fmaf(lk[k], wk, Lm);
           O = fmaf(ak[k], wk, O);
@@ -1154,7 +1165,7 @@ __global__ __launch_bounds__(256) void decode_stream_merge(DecodeArgs a) {
       }
       M = mn;
     }
-    store_out(a.out, a.out_dtype, ((size_t)r * a.n_heads + kvh * G + j) * HD + d, O / Lm);
+    store_out(a.out, a.out_dtype, stream_out_row(a, kvh, r, j) * HD + d, Lm > 0.f ? O / Lm : 0.f);
   }
 }
 
@@ -1209,7 +1220,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
   __shared__ uint4 s_k[2 * KS * kWave];
   __shared__ uint4 s_v[DT * kWave];
   __shared__ int32_t s_wctx[kWindowRows], s_wgpre[kWindowRows];
-  const StreamLayout L = stream_layout(a.rows, a.n_kv_heads, a.group, a.head_dim, a.max_parts);
+  const StreamLayout L = stream_layout(a.rows, a.n_kv_heads, a.cols, a.head_dim, a.max_parts);
   const int32_t *wsi = reinterpret_cast<const int32_t *>(a.ws);
   const int w = blockIdx.x;
   const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
@@ -1229,9 +1240,10 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
     const long long ng_all0 = (long long)a.n_kv_heads * ngk;
     waves = ng_all0 / max(a.cg_min, 1);
     waves = waves < 1 ? 1 : (waves > kStreamWaves ? kStreamWaves : waves);
-    if (w < a.rows && win.ctx[w] == 0) {  // an empty row reads zeros; no slice visits it
-      for (int idx = lane; idx < a.n_heads * a.head_dim; idx += kWave)
-        store_out(a.out, a.out_dtype, (size_t)w * a.n_heads * a.head_dim + idx, 0.f);
+    if (w < a.rows && win.ctx[w] == 0) {  // an empty row reads zeros (all its queries); no slice visits it
+      const int per_row = a.query_len * a.n_heads * a.head_dim;
+      for (int idx = lane; idx < per_row; idx += kWave)
+        store_out(a.out, a.out_dtype, (size_t)w * per_row + idx, 0.f);
     }
     if (ng_all0 == 0 || w >= waves) return;
     const long long st = slice_start(w, ng_all0, waves);
@@ -1252,11 +1264,14 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
   const int total = (int)(slice_start(w + 1, ng_all, waves) - slice_start(w, ng_all, waves));
   cursor_row(c0, win, w, ngk, ng_all, waves);
 
+  // this lane's column: query lr / group of the row's chunk (the only one for
+  // a one-query read), head kv head * group + lr % group
+  const bool colv = lr < a.cols;
+  const int qcol = colv ? lr / a.group : a.query_len - 1;
   auto load_q = [&](const Cursor &c, bf16x8_t *qb) {
 #pragma unroll
     for (int i = 0; i < KS; ++i)
-      qb[i] = lr < a.group ? ld_bf16x8(a.q, (((size_t)c.r * a.n_heads + c.kvh * a.group + lr) * HD + (4 * i + lg) * 8) * 2)
-                           : zero_bf16x8();
+      qb[i] = colv ? ld_bf16x8(a.q, (stream_out_row(a, c.kvh, c.r, lr) * HD + (4 * i + lg) * 8) * 2) : zero_bf16x8();
   };
   bf16x8_t qb[KS];
   load_q(c0, qb);
@@ -1301,7 +1316,9 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
     }
     f32x4_t sacc[2];
     group_scores<HD>(kc, qb, sacc);
-    group_softmax_pv<HD>(sacc, vc, acc, m, l, cscale, c0.n, c0.j * kGroupPositions, lg);
+    // causal inside a chunk: query qcol sees positions below n - query_len + qcol + 1
+    const int cend = max(c0.n - a.query_len + qcol + 1, 0);
+    group_softmax_pv<HD>(sacc, vc, acc, m, l, cscale, cend, c0.n, c0.j * kGroupPositions, lg);
     if (c0.j == c0.ng - 1 || last_group) segment_end<HD>(a, L, c0, acc, m, l, lr, lg);
     if (last_group) break;
     const bool new_row = c1.r != c0.r || c1.kvh != c0.kvh;

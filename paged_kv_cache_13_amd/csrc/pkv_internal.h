@@ -28,6 +28,10 @@ struct DecodeArgs {
   // multi-query read: queries per row, 32-column tiles per (row, kv head),
   // queries per tile, query blocks (one workgroup each) per (row, kv head)
   int32_t query_len, q_tiles, q_per_tile, q_blocks;
+  // stream path: score columns per (kv head, row), (query, head) pairs in
+  // that order: group for the one-query read, query_len * group (<= 16)
+  // for a multi-query read on the stream path
+  int32_t cols;
 };
 
 // Multi-query read: a workgroup of multi_waves(tiles) waves, one 32-column
@@ -63,7 +67,7 @@ __host__ __device__ inline WsLayout ws_layout(int32_t rows, int32_t n_heads, int
 //   first_pos[2 * waves]   (kv head * rows + row, group) where each wave starts
 //   gpre[rows + 1]         exclusive prefix of groups per row
 //   counters[kv * rows]    partial slices written per (kv head, row)
-//   partials[kv * rows * max_parts][slot]  fp32 acc[group][hd], m[group], l[group]
+//   partials[kv * rows * max_parts][slot]  fp32 acc[cols][hd], m[cols], l[cols]
 constexpr int kStreamWaves = 1024;  // one persistent wave per SIMD (4 per CU)
 constexpr int kWindowRows = 256;  // rows a wave keeps (and, if that is all, plans) in LDS
 constexpr int kPlanMaxRows = 8192;
@@ -73,7 +77,7 @@ struct StreamLayout {
   size_t slot_stride;
 };
 __host__ __device__ inline size_t align4(size_t x) { return (x + 3) & ~(size_t)3; }
-__host__ __device__ inline StreamLayout stream_layout(int32_t rows, int32_t n_kv, int32_t group,
+__host__ __device__ inline StreamLayout stream_layout(int32_t rows, int32_t n_kv, int32_t cols,
                                                       int32_t head_dim, int32_t max_parts) {
   StreamLayout L;
   L.hdr = 0;
@@ -81,7 +85,7 @@ __host__ __device__ inline StreamLayout stream_layout(int32_t rows, int32_t n_kv
   L.gpre = L.first_pos + 2 * (size_t)kStreamWaves;
   L.counters = L.gpre + (size_t)rows + 1;
   L.partials = align4(L.counters + (size_t)n_kv * rows);
-  L.slot_stride = align4((size_t)group * (head_dim + 2));
+  L.slot_stride = align4((size_t)cols * (head_dim + 2));
   L.total = L.partials + (size_t)n_kv * rows * max_parts * L.slot_stride;
   return L;
 }

@@ -248,21 +248,28 @@ def test_multi_query_refusals(lib):
 
 def test_multi_query_workspace(lib):
     ws = lambda d, q: lib.pkv_paged_attention_multi_workspace_size(ctypes.byref(d), q)
-    # 64 rows x 8 kv heads x one query block (4 queries: one 32-column tile,
-    # a two-wave workgroup, two per compute unit) = 512 blocks on 512 slots:
-    # a 4096-position table wants 4096-position partitions, capped at 2048,
-    # so it splits in 2: m, l and a 128-float acc per (row, query, head,
-    # partition)
+    # 4 queries x 4 heads per kv head = 16 columns: the stream path, whose
+    # workspace is the one-query read's layout with 16 columns per slot --
+    # header, wave starts, row prefixes, counters, then 33 slices (4-group
+    # minimum over a 128-group table) per (kv head, row) of 16 x (128 + 2)
     d = desc()
-    slots = 64 * 4 * 32 * 2
-    assert ws(d, 4) == (((2 * slots + 3) & ~3) + slots * 128) * 4
+    head = 4 + 2 * 1024 + 65 + 8 * 64
+    head = (head + 3) & ~3
+    assert ws(d, 4) == (head + 8 * 64 * 33 * 16 * 130) * 4
+    # 8 queries (32 columns): the workgroup path.  64 rows x 8 kv heads x one
+    # query block (a two-wave workgroup, two per compute unit) = 512 blocks
+    # on 512 slots: a 4096-position table wants 4096-position partitions,
+    # capped at 2048, so it splits in 2: m, l and a 128-float acc per (row,
+    # query, head, partition)
+    slots = 64 * 8 * 32 * 2
+    assert ws(d, 8) == (((2 * slots + 3) & ~3) + slots * 128) * 4
     # 16 rows: 128 blocks want 1024-position partitions (4 of them)
-    slots16 = 16 * 4 * 32 * 4
-    assert ws(desc(rows=16), 4) == (((2 * slots16 + 3) & ~3) + slots16 * 128) * 4
+    slots16 = 16 * 8 * 32 * 4
+    assert ws(desc(rows=16), 8) == (((2 * slots16 + 3) & ~3) + slots16 * 128) * 4
     # a caller's partition (a multiple of the block size) is rounded up to
     # 32 positions and capped at 4096
-    slots4 = 64 * 4 * 32 * 4
-    assert ws(desc(partition_tokens=1008), 4) == (((2 * slots4 + 3) & ~3) + slots4 * 128) * 4
-    assert ws(desc(partition_tokens=8192), 4) == 0   # capped at 4096: one partition, written directly
-    assert ws(desc(max_blocks_per_row=64, partition_tokens=1024), 4) == 0
+    slots4 = 64 * 8 * 32 * 4
+    assert ws(desc(partition_tokens=1008), 8) == (((2 * slots4 + 3) & ~3) + slots4 * 128) * 4
+    assert ws(desc(partition_tokens=8192), 8) == 0   # capped at 4096: one partition, written directly
+    assert ws(desc(max_blocks_per_row=64, partition_tokens=1024), 8) == 0
     assert ws(desc(dtype=0, out_dtype=0), 4) == 0    # refused descriptors need nothing

@@ -437,9 +437,12 @@ def test_read_many_rows(rows):
 # multi-query read (a chunk of queries per row, causal inside the chunk)
 # ---------------------------------------------------------------------------
 
-def multi_case(rows, H, KV, hd, bs, lo, hi, qlen, seed, value_scale=1.0):
+def multi_case(rows, H, KV, hd, bs, lo, hi, qlen, seed, value_scale=1.0, width=0):
+    # width: block-table width in positions (0: the longest row).  The
+    # library picks the stream path for query_len * group <= 16 from the
+    # table's shape: a wide table over short rows selects it.
     cfg = synth.DecodeConfig("multi", "bf16", rows=rows, n_heads=H, n_kv_heads=KV, head_dim=hd, block_size=bs,
-                             ctx=("uniform", lo, hi), pool=("factor", 1.5), max_ctx=max(hi, bs),
+                             ctx=("uniform", lo, hi), pool=("factor", 1.5), max_ctx=max(hi, bs, width),
                              value_scale=value_scale, seed=seed)
     b = synth.make_batch(cfg, device=DEV)
     g = torch.Generator(device=DEV).manual_seed(seed + 1)
@@ -468,6 +471,23 @@ def multi_oracle(b, q):
 def test_multi_query_read_matches_oracle(H, KV, hd, bs, lo, hi, qlen, part):
     note("multi H=%d KV=%d hd=%d bs=%d q=%d part=%d" % (H, KV, hd, bs, qlen, part))
     b, q = multi_case(5, H, KV, hd, bs, lo, hi, qlen, seed=hd + bs + qlen)
+    check_multi(b, q, part)
+
+
+# query_len * group <= 16 over a wide table: the one-query read's stream
+# path.  Rows cut into short slices (partition_tokens sets the slice
+# minimum), G = 4, 8, 1 and 2.
+@pytest.mark.parametrize("H,KV,hd,bs,lo,hi,qlen,part", [
+    (32, 8, 128, 16, 1, 700, 4, 64), (32, 8, 128, 8, 1, 600, 4, 32), (64, 8, 64, 32, 1, 500, 2, 0),
+    (16, 16, 128, 16, 1, 400, 16, 96), (16, 8, 128, 16, 30, 900, 8, 0), (32, 8, 128, 16, 1, 300, 1, 0),
+])
+def test_multi_query_stream_path_matches_oracle(H, KV, hd, bs, lo, hi, qlen, part):
+    note("multi stream H=%d KV=%d hd=%d bs=%d q=%d part=%d" % (H, KV, hd, bs, qlen, part))
+    b, q = multi_case(5, H, KV, hd, bs, lo, hi, qlen, seed=hd + bs + qlen + 1, width=32768)
+    check_multi(b, q, part)
+
+
+def check_multi(b, q, part):
     got = pkv.paged_attention_multi(q, b.k_pool, b.v_pool, b.block_table, b.context_lens, b.scale,
                                     partition_tokens=part)
     got32 = pkv.paged_attention_multi(q, b.k_pool, b.v_pool, b.block_table, b.context_lens, b.scale,
@@ -479,12 +499,12 @@ def test_multi_query_read_matches_oracle(H, KV, hd, bs, lo, hi, qlen, part):
     assert_close(got32.cpu(), ref, what="multi fp32 out", **TOL[torch.float32])
 
 
-@pytest.mark.parametrize("bs,qlen", [(8, 20), (32, 70)])
-def test_multi_query_ignores_poisoned_slots_bitwise(bs, qlen):
+@pytest.mark.parametrize("bs,qlen,width", [(8, 20, 900), (32, 70, 900), (16, 4, 32768)])  # last: stream path
+def test_multi_query_ignores_poisoned_slots_bitwise(bs, qlen, width):
     # unused table entries point at a NaN block and slots past each row's end
     # hold NaN (P6): the output must not change, bit for bit
     cfg = synth.DecodeConfig("multi", "bf16", rows=5, n_heads=32, n_kv_heads=8, head_dim=128, block_size=bs,
-                             ctx=("uniform", 1, 900), pool=("factor", 1.5), max_ctx=900, seed=61)
+                             ctx=("uniform", 1, 900), pool=("factor", 1.5), max_ctx=width, seed=61)
     clean = synth.make_batch(cfg, device=DEV, poison=False)
     dirty = synth.make_batch(cfg, device=DEV, poison=True)
     assert torch.isnan(dirty.k_pool.float()).any() and torch.isnan(dirty.v_pool.float()).any()
@@ -500,15 +520,16 @@ def test_multi_query_ignores_poisoned_slots_bitwise(bs, qlen):
     assert torch.equal(outs[0], outs[1])
 
 
-def test_multi_query_rows_shorter_than_the_chunk_read_zeros():
-    b, q = multi_case(6, 32, 8, 128, 16, 1, 6, 8, seed=41)
+@pytest.mark.parametrize("qlen,width", [(8, 0), (4, 32768)])  # workgroup path, stream path
+def test_multi_query_rows_shorter_than_the_chunk_read_zeros(qlen, width):
+    b, q = multi_case(6, 32, 8, 128, 16, 1, qlen - 2, qlen, seed=41, width=width)
     got = pkv.paged_attention_multi(q, b.k_pool, b.v_pool, b.block_table, b.context_lens, b.scale)
     torch.cuda.synchronize()
     ref = multi_oracle(b, q)
     assert_close(got.float().cpu(), ref, what="short rows", **TOL[torch.bfloat16])
     for r in range(6):
         n = int(b.ctx_host[r])
-        assert (got[r, :8 - n].float() == 0).all()
+        assert (got[r, :qlen - n].float() == 0).all()
 
 
 def test_multi_query_of_one_matches_the_decode_read():
