@@ -1028,6 +1028,7 @@ __device__ __forceinline__ void group_softmax_pv(const f32x4_t (&sacc)[2], bf16x
 // Output row of stream column `col` of (kv head, row): query col / group,
 // head kv head * group + col % group.
 __device__ __forceinline__ size_t stream_out_row(const DecodeArgs &a, int kvh, int r, int col) {
+  if (a.query_len == 1) return (size_t)r * a.n_heads + kvh * a.group + col;  // no division on the one-query read
   return ((size_t)r * a.query_len + col / a.group) * a.n_heads + kvh * a.group + col % a.group;
 }
 
@@ -1157,8 +1158,9 @@ __global__ __launch_bounds__(256) void decode_stream_merge(DecodeArgs a) {
       O *= a0;
 #pragma unroll
       for (int k = 0; k < kMergeMaxParts; ++k) {
-        if (k < kn && mk[k] != -INFINITY) {  // a slice that saw nothing of this column adds nothing
-          const float wk = exp2_fast(mk[k] - mn);
+        if (k < kn) {
+          // a slice that saw nothing of this column (m = -inf) adds nothing
+          const float wk = mk[k] == -INFINITY ? 0.f : exp2_fast(mk[k] - mn);
           Lm = fmaf(lk[k], wk, Lm);
           O = fmaf(ak[k], wk, O);
         }
