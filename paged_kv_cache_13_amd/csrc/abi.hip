@@ -51,6 +51,8 @@ int32_t default_partition(const pkv_attn_desc *d, int32_t cap) {
   return (int32_t)part;
 }
 
+constexpr int64_t kSmallBatchPairs = 256;   // (kv head, row) pairs
+constexpr int64_t kSmallBatchTable = 4096;  // positions a row's table can hold
 struct Plan {
   int32_t group, partition, max_parts, log2_bs;
   int32_t stream, cg_min;
@@ -82,10 +84,15 @@ int plan_decode(const pkv_attn_desc *d, Plan *pl) {
   pl->ws_bytes = 0;
   // bf16 with head_dim 64/128 runs the balanced stream decomposition when the
   // plan kernel can hold the rows and the group count fits in 31 bits;
-  // everything else runs one workgroup per (partition, kv head, row).
+  // everything else runs one workgroup per (partition, kv head, row).  So
+  // does a small batch over a short table: there the partition kernel's one
+  // launch beats the stream's fixed start-up and merge (8B-shaped layer:
+  // 8 rows x 1k positions 17 vs 23 us, 32 rows x 4k 58 vs 61 us), while long
+  // tables keep the stream's balance (4 rows x 32k positions: 100 vs 128 us).
   const int64_t cap_groups = (cap + pkv::kGroupPositions - 1) / pkv::kGroupPositions;
+  const bool small_batch = (int64_t)d->rows * d->n_kv_heads <= kSmallBatchPairs && cap <= kSmallBatchTable;
   pl->stream = d->dtype == PKV_BF16 && (d->head_dim == 64 || d->head_dim == 128) &&
-               d->rows <= pkv::kPlanMaxRows &&
+               d->rows <= pkv::kPlanMaxRows && !small_batch &&
                cap_groups * d->n_kv_heads * d->rows < (int64_t)INT_MAX;
   if (pl->stream) {
     // slices of at least cg_min groups: the caller's partition length, else

@@ -100,6 +100,18 @@ def test_workspace_size_stream_layout(lib):
     assert ws(lib, rows=9000, max_blocks_per_row=32) == 0
 
 
+def test_small_batches_over_short_tables_take_partitions(lib):
+    # at most 256 (row, kv head) pairs over a table of at most 4096 positions:
+    # the bf16 read uses the partition layout, the same as an fp32 read
+    part = lambda **kw: ws(lib, dtype=0, out_dtype=0, **kw)
+    assert ws(lib, rows=32) == part(rows=32)                      # 256 pairs, 4096 positions
+    assert ws(lib, rows=2, max_blocks_per_row=64) == part(rows=2, max_blocks_per_row=64)
+    # one more position, or one more row, and the stream layout comes back
+    assert ws(lib, rows=32, max_blocks_per_row=257) != part(rows=32, max_blocks_per_row=257)
+    assert ws(lib, rows=33) != part(rows=33)
+    assert ws(lib, rows=33) > 4 * (2 * 1024)  # the stream header is there
+
+
 def attn(lib, d, q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, cl=FAKE, out=FAKE, wsp=FAKE, wsb=1 << 40):
     return lib.pkv_paged_attention(ctypes.byref(d) if d is not None else None, q, kp, vp, bt, cl,
                                    ctypes.c_float(1.0), out, wsp, wsb, None)

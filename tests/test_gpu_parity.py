@@ -167,6 +167,19 @@ def test_read_head_groups(dtype, hd, H, KV):
     assert_close(got.cpu(), ref, what="groups", **TOL[torch.float32])
 
 
+@pytest.mark.parametrize("hd", [64, 128])
+@pytest.mark.parametrize("H,KV", [(4, 4), (8, 4), (12, 4), (16, 4), (64, 4)])
+def test_read_head_groups_wide_table(hd, H, KV):
+    # a few rows in a table wider than the small-batch limit: the bf16 stream
+    # kernel with every group size it packs, padded lanes included
+    cfg = small_cfg("bf16", rows=3, H=H, KV=KV, hd=hd, bs=16, lo=1, hi=3000, seed=H + hd + 1,
+                    max_ctx=8192)
+    b = synth.make_batch(cfg, device=DEV)
+    ref = oracle_read(b)
+    got = gpu_read(b, out_dtype=torch.float32)
+    assert_close(got.cpu(), ref, what="groups wide", **TOL[torch.float32])
+
+
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("bs", [8, 16, 32])
 @pytest.mark.parametrize("part", [0, 1, 2, 8, 64, 10 ** 6])
@@ -247,9 +260,10 @@ def test_read_is_deterministic(name):
         assert torch.equal(first, gpu_read(b, out_dtype=torch.float32))
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
-def test_read_ignores_poisoned_slots_bitwise(dtype):
-    cfg = small_cfg(dtype, rows=6, H=8, KV=2, hd=128, bs=16, lo=1, hi=1200, seed=9)
+@pytest.mark.parametrize("dtype,width", [("f32", 0), ("bf16", 0), ("bf16", 8192)])
+def test_read_ignores_poisoned_slots_bitwise(dtype, width):
+    cfg = small_cfg(dtype, rows=6, H=8, KV=2, hd=128, bs=16, lo=1, hi=1200, seed=9,
+                    max_ctx=width or None)
     clean = synth.make_batch(cfg, device=DEV, poison=False)
     dirty = synth.make_batch(cfg, device=DEV, poison=True)
     assert torch.isnan(dirty.k_pool.float()).any()
@@ -373,11 +387,13 @@ def test_decode_step_replays_from_a_graph():
 # closed forms on the GPU path
 # ---------------------------------------------------------------------------
 
-@pytest.mark.parametrize("dtype,hd", [("bf16", 128), ("bf16", 64), ("bf16", 16), ("f32", 128)])
-def test_read_constant_values_give_that_constant(dtype, hd):
+@pytest.mark.parametrize("dtype,hd,width", [("bf16", 128, 0), ("bf16", 64, 0), ("bf16", 16, 0),
+                                            ("f32", 128, 0), ("bf16", 128, 8192), ("bf16", 64, 8192)])
+def test_read_constant_values_give_that_constant(dtype, hd, width):
     # V == c everywhere: every softmax weighting returns c; the weights in the
     # numerator and the sum in the denominator must agree
-    cfg = small_cfg(dtype, rows=8, H=32, KV=8, hd=hd, bs=16, lo=1, hi=3000, seed=21)
+    cfg = small_cfg(dtype, rows=8, H=32, KV=8, hd=hd, bs=16, lo=1, hi=3000, seed=21,
+                    max_ctx=width or None)
     b = synth.make_batch(cfg, device=DEV)
     c = torch.linspace(-2, 2, hd, device=DEV).to(b.v_pool.dtype)  # exact in bf16
     b.v_pool.copy_(c[None, None, :, None].expand_as(b.v_pool))
@@ -397,13 +413,16 @@ def test_read_zero_query_gives_mean_of_values(dtype, hd):
     assert_close(got, ref, what="zero query", **TOL[torch.float32])
 
 
+@pytest.mark.parametrize("width", [0, 8192])  # 0: table as wide as the longest row
 @pytest.mark.parametrize("bs", [8, 16, 32])
 @pytest.mark.parametrize("hd", [64, 128])
-def test_read_edge_lengths_bf16(bs, hd):
+def test_read_edge_lengths_bf16(bs, hd, width):
     # the bf16 path splits work over the whole batch: empty rows, one-position
-    # rows, block-boundary rows and one row filling its table, in one batch
+    # rows, block-boundary rows and one row filling its table, in one batch.
+    # A small batch over a short table is read by the partition kernel, over
+    # a wide one by the stream kernel: both are run.
     lens = [0, 1, 31, 32, 33, bs - 1, bs, bs + 1, 0, 511, 512, 513, 2000, 16 * 64]
-    cap = max(lens)
+    cap = max(lens + [width])
     cfg = synth.DecodeConfig("edge16", "bf16", rows=len(lens), n_heads=16, n_kv_heads=4, head_dim=hd,
                              block_size=bs, ctx=("fixed", tuple(lens)), pool=("factor", 1.5),
                              max_ctx=cap, seed=6)
