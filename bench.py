@@ -405,9 +405,11 @@ def main():
                    "n_kv_heads": cfg.n_kv_heads, "head_dim": cfg.head_dim, "block_size": bs,
                    "context_lens": "uniform[512,4096]" if cfg.name == "llama3_8b_layer" else str(cfg.ctx),
                    "sum_ctx": int(batch.ctx_host.sum()), "num_blocks": batch.num_blocks,
-                   "partition_tokens": args.partition or 512},
+                   "partition_tokens": args.partition or "library default"},
         "read_us": round(read_us, 2),
         "read_us_median": round(float(np.median(read_ms)) * 1e3, 2),
+        "read_us_p10": round(float(np.percentile(read_ms, 10)) * 1e3, 2),
+        "read_us_p90": round(float(np.percentile(read_ms, 90)) * 1e3, 2),
         "read_us_flushed": round(float(np.median(fl_ms)) * 1e3, 2) if fl_ms else None,
         "read_pct_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
         "read_bytes": rb,
