@@ -1,18 +1,20 @@
 #!/usr/bin/env python3
 """Benchmark of one decode step of the paged KV cache on one MI355X.
 
-A step is the whole hot path over one batch: the slot-mapping scatter of each
-row's new token K/V into the pool, then the paged decode read of every row
-(GQA heads, split-context partitions + merge).  The workload is a
+A step is the whole hot path over one batch, as one library call
+(pkv_decode_step): the slot-mapping scatter of each row's new token K/V into
+the pool, then the paged decode read of every row (GQA heads, split-context
+partitions + merge); the stream read appends the tokens itself.  The workload is a
 Llama-3-8B-shaped attention layer: 64 rows, 32 query heads, 8 kv heads,
 head_dim 128, bf16 pool of 16-position blocks, context lengths uniform in
 [512, 4096], block tables drawn from a 1.5x pool.  Every input is synthetic
 and seeded; inputs are resident in HBM before timing starts.
 
 Prints one JSON line: whole-step HBM throughput (algorithmic bytes / step
-time), the read's µs per call and its fraction of MI355X's 8 TB/s, the read
-kernel timed with HIP events on the stream it runs on, and the CPU oracle
-timed on this host as a reported baseline.
+time, wall clock over the timed steps), the read's µs per call and its
+fraction of MI355X's 8 TB/s (the read alone, called as many times again,
+each call bracketed by HIP events on the stream it runs on), and the CPU
+oracle timed on this host as a reported baseline.
 """
 import argparse
 import hashlib
@@ -337,8 +339,10 @@ def main():
     wsz = pkv.workspace_size(batch.q, batch.k_pool, batch.block_table, partition_tokens=args.partition)
     ws = torch.empty(max(wsz, 1), dtype=torch.uint8, device=dev)
 
-    def scatter():
-        pkv.reshape_and_cache(new_k, new_v, slots, batch.k_pool, batch.v_pool)
+    def step():  # one call: append every row's new token, then read
+        pkv.decode_step(batch.q, new_k, new_v, slots, batch.k_pool, batch.v_pool, batch.block_table,
+                        batch.context_lens, batch.scale, out=out, workspace=ws,
+                        partition_tokens=args.partition)
 
     def read():
         pkv.paged_attention_into(batch.q, batch.k_pool, batch.v_pool, batch.block_table,
@@ -347,21 +351,26 @@ def main():
 
     stream = torch.cuda.current_stream(dev)
     for _ in range(args.warmup):
-        scatter()
-        read()
+        step()
     torch.cuda.synchronize()
 
+    # the timed steps: wall clock over K back-to-back steps
     K = args.steps
     ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(K):
-        scatter()
+        step()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    # the read alone, K calls, each bracketed by HIP events on its stream
+    for _ in range(args.warmup):
+        read()
+    for i in range(K):
         ev[i][0].record(stream)
         read()
         ev[i][1].record(stream)
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
     read_ms = np.array([a.elapsed_time(b) for a, b in ev])
 
     # reads with the Infinity Cache flushed (a 512 MiB write) before each

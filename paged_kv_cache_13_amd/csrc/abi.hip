@@ -208,7 +208,9 @@ int check_attention(const pkv_attn_desc *d, const void *q, const void *k_pool, c
 
 int launch_attention(const pkv_attn_desc *d, const Plan &pl, const void *q, const void *k_pool,
                      const void *v_pool, const int32_t *block_table, const int32_t *context_lens,
-                     float scale, void *out, void *workspace, hipStream_t stream) {
+                     float scale, void *out, void *workspace, hipStream_t stream,
+                     const void *k_new = nullptr, const void *v_new = nullptr,
+                     const int64_t *slot_new = nullptr) {
   if (d->rows == 0) return PKV_OK;
   pkv::DecodeArgs a = {};
   a.q = q;
@@ -237,6 +239,9 @@ int launch_attention(const pkv_attn_desc *d, const Plan &pl, const void *q, cons
   a.scale = scale;
   a.query_len = 1;
   a.cols = pl.group;
+  a.k_new = k_new;
+  a.v_new = v_new;
+  a.slot_new = slot_new;
   return pkv::launch_decode(a, stream) == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 
@@ -416,6 +421,11 @@ int pkv_decode_step(const pkv_attn_desc *d, const void *k_new, const void *v_new
   if (st != PKV_OK) return st;
   if (d->rows == 0) return PKV_OK;
   const hipStream_t hs = static_cast<hipStream_t>(stream);
+  // The stream read appends the new tokens itself (one launch less); the
+  // other read kernels run after a scatter.
+  if (pl.stream)
+    return launch_attention(d, pl, q, k_pool, v_pool, block_table, context_lens, scale, out, workspace, hs,
+                            k_new, v_new, slot_mapping);
   if (pkv::launch_scatter(k_new, v_new, slot_mapping, d->rows, k_pool, v_pool, d->num_blocks,
                           d->block_size, d->n_kv_heads, d->head_dim, d->dtype, hs) != hipSuccess)
     return PKV_ERR_LAUNCH;

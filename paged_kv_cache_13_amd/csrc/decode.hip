@@ -721,6 +721,24 @@ __device__ __forceinline__ long long slice_of(long long pos, long long total, lo
   return ((pos + 1) * waves - 1) / total;
 }
 
+// A row with no positions that still brings a token: appended whole (every
+// kv head) by the wave that zero-fills the row, as the scatter would.
+__device__ __forceinline__ void append_empty_row(const DecodeArgs &a, int r, int t0, int nthreads) {
+  const int64_t s = a.slot_new[r];
+  if (s < 0 || s >= a.num_blocks * a.block_size) return;
+  const int64_t blk = s >> a.log2_bs, off = s & (a.block_size - 1);
+  const int per = a.n_kv_heads * a.head_dim;
+  const uint16_t *kn = static_cast<const uint16_t *>(a.k_new) + (size_t)r * per;
+  const uint16_t *vn = static_cast<const uint16_t *>(a.v_new) + (size_t)r * per;
+  uint16_t *kp = static_cast<uint16_t *>(const_cast<void *>(a.k_pool));
+  uint16_t *vp = static_cast<uint16_t *>(const_cast<void *>(a.v_pool));
+  for (int e = t0; e < per; e += nthreads) {
+    const int h = e / a.head_dim, d = e - h * a.head_dim;
+    kp[((((size_t)blk * a.n_kv_heads + h) << a.log2_bs) + off) * a.head_dim + d] = kn[e];
+    vp[((((size_t)blk * a.n_kv_heads + h) * a.head_dim + d) << a.log2_bs) + off] = vn[e];
+  }
+}
+
 __global__ __launch_bounds__(1024) void decode_plan(DecodeArgs a) {
   __shared__ int32_t s_gpre[kPlanMaxRows + 1];
   __shared__ int32_t s_sum[1024];
@@ -740,6 +758,7 @@ __global__ __launch_bounds__(1024) void decode_plan(DecodeArgs a) {
     if (n == 0) {  // an empty row reads zeros (all its queries); no wave visits it
       const size_t per_row = (size_t)a.query_len * a.n_heads * a.head_dim;
       for (size_t idx = 0; idx < per_row; ++idx) store_out(a.out, a.out_dtype, (size_t)r * per_row + idx, 0.f);
+      if (a.slot_new) append_empty_row(a, r, 0, 1);
     }
   }
   s_sum[tid] = local;
@@ -1216,6 +1235,81 @@ __device__ __forceinline__ void stage_group(uint4 *s_k, uint4 *s_v, const Decode
                                      (void __attribute__((address_space(3))) *)(s_v + dt * kWave), 16, 0, kStreamingLoad);
 }
 
+// The decode step's new token, appended inside the read.  Each (kv head,
+// row) has one wave that reads its last group, which holds the new token at
+// position n - 1; that wave loads the token's K and V row (one group ahead,
+// with the next group's staging), and once the group's tile has landed in
+// LDS it stores the token into its pool slot and over the tile's (stale)
+// copy of that position, before the tile is read.  No other wave reads the
+// slot in this call, so the read sees exactly what a scatter followed by a
+// read would.  Slots that are negative or past the pool are skipped, as the
+// scatter skips them.
+template <int HD>
+struct Append {
+  bool pending;        // wave-uniform: the group computed next holds a new token
+  int p;               // its position in that group
+  int64_t slot;        // loaded by every lane, read after the wait
+  bf16x8_t k[HD / 32]; // lanes lr == kl(p): K dims 32 i + 8 lg .. + 8
+  uint16_t v[HD / 16]; // lanes lg == p / 8: V dims 16 dt + lr
+};
+
+__device__ __forceinline__ int append_k_lane(int p) { return ((p >> 3) << 2) | (p & 3); }
+
+template <int HD>
+__device__ __forceinline__ void append_load(Append<HD> &A, const DecodeArgs &a, const Cursor &c, int lr, int lg) {
+  constexpr int KS = HD / 32, DT = HD / 16;
+  A.pending = a.slot_new != nullptr && c.j == c.ng - 1;
+  if (!A.pending) return;
+  A.p = c.n - 1 - c.j * kGroupPositions;
+  A.slot = a.slot_new[c.r];
+  const size_t base = ((size_t)c.r * a.n_kv_heads + c.kvh) * HD;
+  if (lr == append_k_lane(A.p)) {
+#pragma unroll
+    for (int i = 0; i < KS; ++i) A.k[i] = ld_bf16x8(a.k_new, (base + i * 32 + lg * 8) * 2);
+  }
+  if (lg == (A.p >> 3)) {
+    const uint16_t *vn = static_cast<const uint16_t *>(a.v_new) + base + lr;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) A.v[dt] = vn[dt * 16];
+  }
+}
+
+// After the group's tile has landed, before it is read.  The staging lane
+// layout: K tile tt row 8 (lr / 4) + 4 tt + lr % 4 holds dims 32 i + 8 lg in
+// slot (tt * KS + i) * 64 + lane; V slot dt * 64 + lane holds dim 16 dt + lr
+// at positions 8 lg .. 8 lg + 7.
+template <int HD, int BS>
+__device__ __forceinline__ void append_apply(const Append<HD> &A, const DecodeArgs &a, const Cursor &c, uint4 *s_k,
+                                             uint4 *s_v, int lane, int lr, int lg) {
+  constexpr int KS = HD / 32, DT = HD / 16;
+  constexpr int LOG2_BS = BS == 8 ? 3 : (BS == 16 ? 4 : 5);
+  const int64_t s = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(A.slot >> 32)) << 32) |
+                              (uint32_t)__builtin_amdgcn_readfirstlane((int)A.slot));
+  if (s < 0 || s >= a.num_blocks * BS) return;
+  const int64_t blk = s >> LOG2_BS;
+  const int off = (int)(s & (BS - 1)), p = A.p;
+  if (lr == append_k_lane(p)) {
+    const int tt = (p >> 2) & 1;
+    uint16_t *kp = static_cast<uint16_t *>(const_cast<void *>(a.k_pool)) +
+                   ((((size_t)blk * a.n_kv_heads + c.kvh) << LOG2_BS) + off) * HD + lg * 8;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) {
+      const uint4 x = __builtin_bit_cast(uint4, A.k[i]);
+      s_k[(tt * KS + i) * kWave + lane] = x;
+      *reinterpret_cast<uint4 *>(kp + i * 32) = x;
+    }
+  }
+  if (lg == (p >> 3)) {
+    uint16_t *vp = static_cast<uint16_t *>(const_cast<void *>(a.v_pool)) +
+                   ((((size_t)blk * a.n_kv_heads + c.kvh) * HD + lr) << LOG2_BS) + off;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) {
+      reinterpret_cast<uint16_t *>(s_v + dt * kWave + lane)[p & 7] = A.v[dt];
+      vp[(size_t)dt * 16 * BS] = A.v[dt];
+    }
+  }
+}
+
 template <int HD, int BS>
 __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void decode_stream(DecodeArgs a) {
   constexpr int KS = HD / 32, DT = HD / 16;
@@ -1246,6 +1340,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
       const int per_row = a.query_len * a.n_heads * a.head_dim;
       for (int idx = lane; idx < per_row; idx += kWave)
         store_out(a.out, a.out_dtype, (size_t)w * per_row + idx, 0.f);
+      if (a.slot_new) append_empty_row(a, w, lane, kWave);
     }
     if (ng_all0 == 0 || w >= waves) return;
     const long long st = slice_start(w, ng_all0, waves);
@@ -1294,6 +1389,8 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
     stage_group<HD, BS>(s_k, s_v, a, c0, ids0, lane, lr, lg);
   }
   ids1 = load_ids<BS>(a, c1, lr, lg);
+  Append<HD> ap;
+  append_load<HD>(ap, a, c0, lr, lg);
 
   bf16x8_t kc[2][KS], vc[DT];
   while (true) {
@@ -1302,6 +1399,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
     // itself, so the wait is explicit and fenced against reordering.
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     asm volatile("" ::: "memory");
+    if (ap.pending) append_apply<HD, BS>(ap, a, c0, s_k, s_v, lane, lr, lg);
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
@@ -1315,6 +1413,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
     if (!last_group) {
       ids2 = load_ids<BS>(a, c2, lr, lg);
       stage_group<HD, BS>(s_k, s_v, a, c1, ids1, lane, lr, lg);
+      append_load<HD>(ap, a, c1, lr, lg);
     }
     f32x4_t sacc[2];
     group_scores<HD>(kc, qb, sacc);

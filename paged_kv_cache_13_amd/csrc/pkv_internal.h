@@ -32,6 +32,11 @@ struct DecodeArgs {
   // that order: group for the one-query read, query_len * group (<= 16)
   // for a multi-query read on the stream path
   int32_t cols;
+  // decode step fused into the stream read: the step's new token of every
+  // row (k_new, v_new [rows, n_kv_heads, head_dim], slot_new [rows]),
+  // appended by the read itself.  Null: a plain read.
+  const void *k_new, *v_new;
+  const int64_t *slot_new;
 };
 
 // Multi-query read: a workgroup of multi_waves(tiles) waves, one 32-column

@@ -315,30 +315,53 @@ def test_decode_run_sweep(rows, bs):
 # one-call decode step, and its replay from a captured HIP graph
 # ---------------------------------------------------------------------------
 
-def test_decode_step_equals_scatter_then_read():
-    run = synth.DecodeRun(rows=32, block_size=16, prompt=200, steps=8, device=DEV, seed=21)
+def equal_nan(a, b):
+    return torch.equal(torch.isnan(a), torch.isnan(b)) and torch.equal(a.nan_to_num(0.0), b.nan_to_num(0.0))
+
+
+@pytest.mark.parametrize("rows,bs,prompt,hd", [
+    (32, 16, 200, 128),  # 256 (row, kv head) pairs, short table: partition kernel after a scatter
+    (64, 16, 200, 128),  # stream kernel appending the tokens itself: positions 8.. of a group
+    (64, 8, 29, 128),    # new tokens at the last position of a group, then the first ones
+    (40, 32, 61, 64),    # head_dim 64
+    (300, 16, 45, 128),  # more rows than a wave plans for: the plan kernel runs first
+])
+def test_decode_step_equals_scatter_then_read(rows, bs, prompt, hd):
+    # bitwise: the one-call step (fused or not) against a scatter then a read.
+    # Every third step some rows bring no token (slot -1): they read what the
+    # pool holds, both ways.
+    run = synth.DecodeRun(rows=rows, block_size=bs, prompt=prompt, steps=6, head_dim=hd, device=DEV,
+                          seed=21 + rows + bs)
     k, v, slots = run.prefill()
     pkv.reshape_and_cache(k, v, slots, run.k_pool, run.v_pool)
     kp2, vp2 = run.k_pool.clone(), run.v_pool.clone()
-    note("decode step vs scatter + read")
-    for _ in range(run.steps):
+    note("decode step vs scatter + read rows=%d bs=%d prompt=%d hd=%d" % (rows, bs, prompt, hd))
+    skipped = torch.zeros(rows, dtype=torch.bool)
+    for step in range(run.steps):
         q, kn, vn, sl = run.step()
+        if step % 3 == 2:
+            sl = sl.clone()
+            sl[step::5] = -1
+            skipped[step::5] = True
         bt, cl = run.block_table(), run.context_lens()
         a = pkv.decode_step(q, kn, vn, sl, run.k_pool, run.v_pool, bt, cl, run.scale)
         pkv.reshape_and_cache(kn, vn, sl, kp2, vp2)
         b = pkv.paged_attention(q, kp2, vp2, bt, cl, run.scale)
         torch.cuda.synchronize()
-        assert torch.equal(a, b)
-    assert torch.equal(run.k_pool.view(torch.int16), kp2.view(torch.int16))
-    assert torch.equal(run.v_pool.view(torch.int16), vp2.view(torch.int16))
+        assert equal_nan(a, b), "step %d" % step
+        assert torch.equal(run.k_pool.view(torch.int16), kp2.view(torch.int16))
+        assert torch.equal(run.v_pool.view(torch.int16), vp2.view(torch.int16))
+    # rows that never skipped a token read only what was written
+    assert torch.isfinite(a.float().cpu()[~skipped]).all()
 
 
-def test_decode_step_replays_from_a_graph():
+@pytest.mark.parametrize("rows", [24, 48])  # scatter + partition kernel; stream kernel appending itself
+def test_decode_step_replays_from_a_graph(rows):
     # capture once; every later step copies its inputs into the captured
     # tensors and replays.  Lengths grow and blocks are allocated between
     # replays, the launch shape stays rows-only.  Each replay is checked
     # against the same step run eagerly on a second copy of the pools.
-    rows, bs = 24, 16
+    bs = 16
     run = synth.DecodeRun(rows=rows, block_size=bs, prompt=120, steps=24, device=DEV, seed=22)
     k, v, slots = run.prefill()
     pkv.reshape_and_cache(k, v, slots, run.k_pool, run.v_pool)
