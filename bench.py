@@ -171,8 +171,13 @@ def other_workloads(dev, stream):
                 steps.append((q, kn, vn, sl, bt, cl, ws, run.ctx_host.copy()))
             stats = pkv.ReadCounters("streamed", block=bs)
             out = torch.empty(rows, run.n_heads, run.head_dim, dtype=torch.bfloat16, device=dev)
-            t_sc, t_rd, t_rect, rbytes = [], [], [], 0
+            t_sc, t_rd, t_step, t_rect, rbytes = [], [], [], [], 0
             for q, kn, vn, sl, bt, cl, ws, ctx in steps:
+                # the step as one call first, then again as a scatter and a read
+                # (writing the same token to the same slot again): the later
+                # calls find more of the step's data in the Infinity Cache
+                t_step.append(_timed(lambda: pkv.decode_step(q, kn, vn, sl, run.k_pool, run.v_pool, bt, cl,
+                                                             run.scale, out=out, workspace=ws), stream, 1)[0])
                 t_sc.append(_timed(lambda: pkv.reshape_and_cache(kn, vn, sl, run.k_pool, run.v_pool), stream, 1)[0])
                 t_rd.append(_timed(lambda: pkv.paged_attention_into(q, run.k_pool, run.v_pool, bt, cl, run.scale,
                                                                      out, ws), stream, 1)[0])
@@ -187,6 +192,7 @@ def other_workloads(dev, stream):
                 "prefill_scatter_GB/s": round(harness.scatter_bytes(rows * run.prompt, run.n_kv_heads,
                                                                     run.head_dim, 2) / (pre_us * 1e-6) / 1e9, 1),
                 "step_scatter_us": round(float(np.mean(t_sc)), 2), "step_read_us": round(rd, 2),
+                "step_one_call_us": round(float(np.mean(t_step)), 2),
                 "step_read_GB/s": round(rbytes / run.steps / (rd * 1e-6) / 1e9, 1),
                 "step_rect_us": round(float(np.mean(t_rect)), 2),
                 "rect_over_paged": round(float(np.mean(t_rect)) / rd, 2),

@@ -421,9 +421,10 @@ int pkv_decode_step(const pkv_attn_desc *d, const void *k_new, const void *v_new
   if (st != PKV_OK) return st;
   if (d->rows == 0) return PKV_OK;
   const hipStream_t hs = static_cast<hipStream_t>(stream);
-  // The stream read appends the new tokens itself (one launch less); the
-  // other read kernels run after a scatter.
-  if (pl.stream)
+  // The bf16 reads with head_dim 64 / 128 (stream and partition kernels)
+  // append the new tokens themselves (one launch less); the other read
+  // kernels run after a scatter.
+  if (d->dtype == PKV_BF16 && (d->head_dim == 64 || d->head_dim == 128))
     return launch_attention(d, pl, q, k_pool, v_pool, block_table, context_lens, scale, out, workspace, hs,
                             k_new, v_new, slot_mapping);
   if (pkv::launch_scatter(k_new, v_new, slot_mapping, d->rows, k_pool, v_pool, d->num_blocks,

@@ -564,6 +564,114 @@ __device__ __forceinline__ void mfma_compute(MfmaTiles<HD> &T, const bf16x8_t *q
   }
 }
 
+// The decode step's new token, appended inside the read.  Each (kv head,
+// row) has one wave that reads the group holding the row's new token (its
+// last position, n - 1); that wave loads the token's K and V row ahead of
+// time, and once the group has been loaded it stores the token into its
+// pool slot and over the loaded (stale) copy of that position, before the
+// group is used.  No other wave reads the slot in this call, so the read
+// sees exactly what a scatter followed by a read would.  Slots that are
+// negative or past the pool are skipped, as the scatter skips them.
+//
+// Lane layout of a loaded group (the same for the stream kernel's LDS tile
+// and the partition kernel's registers): K tile tt, row 8 (lr / 4) + 4 tt +
+// lr % 4, dims 32 i + 8 lg .. + 8 in K fragment (tt, i) of lane (lr, lg);
+// V fragment dt of lane (lr, lg): dim 16 dt + lr at positions 8 lg .. + 7.
+template <int HD>
+struct Append {
+  bool pending;        // wave-uniform: the token's group is computed next
+  int p;               // the token's position in its group
+  int64_t slot;        // loaded by every lane, read after the wait
+  bf16x8_t k[HD / 32]; // lanes lr == append_k_lane(p): K dims 32 i + 8 lg .. + 8
+  uint16_t v[HD / 16]; // lanes lg == p / 8: V dims 16 dt + lr
+};
+
+__device__ __forceinline__ int append_k_lane(int p) { return ((p >> 3) << 2) | (p & 3); }
+
+template <int HD>
+__device__ __forceinline__ void append_fetch(Append<HD> &A, const DecodeArgs &a, int r, int kvh, int p, int lr,
+                                             int lg) {
+  constexpr int KS = HD / 32, DT = HD / 16;
+  A.p = p;
+  A.slot = a.slot_new[r];
+  const size_t base = ((size_t)r * a.n_kv_heads + kvh) * HD;
+  if (lr == append_k_lane(p)) {
+#pragma unroll
+    for (int i = 0; i < KS; ++i) A.k[i] = ld_bf16x8(a.k_new, (base + i * 32 + lg * 8) * 2);
+  }
+  if (lg == (p >> 3)) {
+    const uint16_t *vn = static_cast<const uint16_t *>(a.v_new) + base + lr;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) A.v[dt] = vn[dt * 16];
+  }
+}
+
+// The slot, once the fetch has landed; -1 when the token is skipped.
+template <int BS>
+__device__ __forceinline__ int64_t append_slot(int64_t slot, const DecodeArgs &a) {
+  const int64_t s = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(slot >> 32)) << 32) |
+                              (uint32_t)__builtin_amdgcn_readfirstlane((int)slot));
+  return (s < 0 || s >= a.num_blocks * BS) ? -1 : s;
+}
+
+template <int HD, int BS>
+__device__ __forceinline__ void append_store_pool(const Append<HD> &A, const DecodeArgs &a, int kvh, int64_t s, int lr,
+                                                  int lg) {
+  constexpr int KS = HD / 32, DT = HD / 16;
+  constexpr int LOG2_BS = BS == 8 ? 3 : (BS == 16 ? 4 : 5);
+  const int64_t blk = s >> LOG2_BS;
+  const int off = (int)(s & (BS - 1));
+  if (lr == append_k_lane(A.p)) {
+    uint16_t *kp = static_cast<uint16_t *>(const_cast<void *>(a.k_pool)) +
+                   ((((size_t)blk * a.n_kv_heads + kvh) << LOG2_BS) + off) * HD + lg * 8;
+#pragma unroll
+    for (int i = 0; i < KS; ++i) *reinterpret_cast<uint4 *>(kp + i * 32) = __builtin_bit_cast(uint4, A.k[i]);
+  }
+  if (lg == (A.p >> 3)) {
+    uint16_t *vp = static_cast<uint16_t *>(const_cast<void *>(a.v_pool)) +
+                   ((((size_t)blk * a.n_kv_heads + kvh) * HD + lr) << LOG2_BS) + off;
+#pragma unroll
+    for (int dt = 0; dt < DT; ++dt) vp[(size_t)dt * 16 * BS] = A.v[dt];
+  }
+}
+
+// Partition kernel: one kv head's new token of row r, stored into its pool
+// slot by threads t0, t0 + nthreads, ... (skipped like the scatter skips).
+__device__ __forceinline__ void append_store_row(const DecodeArgs &a, int r, int kvh, int t0, int nthreads) {
+  const int64_t s = a.slot_new[r];
+  if (s < 0 || s >= a.num_blocks * a.block_size) return;
+  const int64_t blk = s >> a.log2_bs, off = s & (a.block_size - 1);
+  const size_t src = ((size_t)r * a.n_kv_heads + kvh) * a.head_dim;
+  const uint16_t *kn = static_cast<const uint16_t *>(a.k_new) + src;
+  const uint16_t *vn = static_cast<const uint16_t *>(a.v_new) + src;
+  uint16_t *kp = static_cast<uint16_t *>(const_cast<void *>(a.k_pool)) +
+                 ((((size_t)blk * a.n_kv_heads + kvh) << a.log2_bs) + off) * a.head_dim;
+  uint16_t *vp = static_cast<uint16_t *>(const_cast<void *>(a.v_pool)) +
+                 ((((size_t)blk * a.n_kv_heads + kvh) * a.head_dim) << a.log2_bs) + off;
+  for (int d = t0; d < a.head_dim; d += nthreads) {
+    kp[d] = kn[d];
+    vp[(size_t)d << a.log2_bs] = vn[d];
+  }
+}
+
+// A row with no positions that still brings a token: appended whole (every
+// kv head) by the wave that zero-fills the row, as the scatter would.
+__device__ __forceinline__ void append_empty_row(const DecodeArgs &a, int r, int t0, int nthreads) {
+  const int64_t s = a.slot_new[r];
+  if (s < 0 || s >= a.num_blocks * a.block_size) return;
+  const int64_t blk = s >> a.log2_bs, off = s & (a.block_size - 1);
+  const int per = a.n_kv_heads * a.head_dim;
+  const uint16_t *kn = static_cast<const uint16_t *>(a.k_new) + (size_t)r * per;
+  const uint16_t *vn = static_cast<const uint16_t *>(a.v_new) + (size_t)r * per;
+  uint16_t *kp = static_cast<uint16_t *>(const_cast<void *>(a.k_pool));
+  uint16_t *vp = static_cast<uint16_t *>(const_cast<void *>(a.v_pool));
+  for (int e = t0; e < per; e += nthreads) {
+    const int h = e / a.head_dim, d = e - h * a.head_dim;
+    kp[((((size_t)blk * a.n_kv_heads + h) << a.log2_bs) + off) * a.head_dim + d] = kn[e];
+    vp[((((size_t)blk * a.n_kv_heads + h) * a.head_dim + d) << a.log2_bs) + off] = vn[e];
+  }
+}
+
 template <int HD, int BS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_partition_mfma(DecodeArgs a) {
   constexpr int KS = HD / 32, DT = HD / 16, GT = 32;
@@ -587,6 +695,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         const int j = idx / HD, d = idx % HD;
         store_out(a.out, a.out_dtype, ((size_t)r * a.n_heads + g * group + j) * HD + d, 0.f);
       }
+      if (n == 0 && g == 0 && a.slot_new) append_empty_row(a, r, tid, kThreads);
     }
     return;
   }
@@ -611,6 +720,17 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     qb[i] = lr < group
                 ? ld_bf16x8(a.q, (((size_t)r * a.n_heads + g * group + lr) * HD + (4 * i + lg) * 8) * 2)
                 : zero_bf16x8();
+  // A decode step's new token (position n - 1) in this partition: stored
+  // into its pool slot before any K/V of the partition is loaded; the
+  // stores complete, and a workgroup-scope fence and the barrier order them
+  // before every wave's loads (the waves share one vector L1).  The loop then reads it from
+  // the pool like any other position: the same bits as a scatter followed
+  // by a read.
+  if (a.slot_new != nullptr && n - 1 < end) {
+    append_store_row(a, r, g, tid, kThreads);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores have completed
+  }
+  __threadfence_block();
   __syncthreads();
 
   const float c = a.scale * kLog2e;
@@ -719,24 +839,6 @@ __device__ __forceinline__ long long slice_start(long long w, long long total, l
 // The slice holding group `pos`: the largest w with slice_start(w) <= pos.
 __device__ __forceinline__ long long slice_of(long long pos, long long total, long long waves) {
   return ((pos + 1) * waves - 1) / total;
-}
-
-// A row with no positions that still brings a token: appended whole (every
-// kv head) by the wave that zero-fills the row, as the scatter would.
-__device__ __forceinline__ void append_empty_row(const DecodeArgs &a, int r, int t0, int nthreads) {
-  const int64_t s = a.slot_new[r];
-  if (s < 0 || s >= a.num_blocks * a.block_size) return;
-  const int64_t blk = s >> a.log2_bs, off = s & (a.block_size - 1);
-  const int per = a.n_kv_heads * a.head_dim;
-  const uint16_t *kn = static_cast<const uint16_t *>(a.k_new) + (size_t)r * per;
-  const uint16_t *vn = static_cast<const uint16_t *>(a.v_new) + (size_t)r * per;
-  uint16_t *kp = static_cast<uint16_t *>(const_cast<void *>(a.k_pool));
-  uint16_t *vp = static_cast<uint16_t *>(const_cast<void *>(a.v_pool));
-  for (int e = t0; e < per; e += nthreads) {
-    const int h = e / a.head_dim, d = e - h * a.head_dim;
-    kp[((((size_t)blk * a.n_kv_heads + h) << a.log2_bs) + off) * a.head_dim + d] = kn[e];
-    vp[((((size_t)blk * a.n_kv_heads + h) * a.head_dim + d) << a.log2_bs) + off] = vn[e];
-  }
 }
 
 __global__ __launch_bounds__(1024) void decode_plan(DecodeArgs a) {
@@ -1235,78 +1337,30 @@ __device__ __forceinline__ void stage_group(uint4 *s_k, uint4 *s_v, const Decode
                                      (void __attribute__((address_space(3))) *)(s_v + dt * kWave), 16, 0, kStreamingLoad);
 }
 
-// The decode step's new token, appended inside the read.  Each (kv head,
-// row) has one wave that reads its last group, which holds the new token at
-// position n - 1; that wave loads the token's K and V row (one group ahead,
-// with the next group's staging), and once the group's tile has landed in
-// LDS it stores the token into its pool slot and over the tile's (stale)
-// copy of that position, before the tile is read.  No other wave reads the
-// slot in this call, so the read sees exactly what a scatter followed by a
-// read would.  Slots that are negative or past the pool are skipped, as the
-// scatter skips them.
-template <int HD>
-struct Append {
-  bool pending;        // wave-uniform: the group computed next holds a new token
-  int p;               // its position in that group
-  int64_t slot;        // loaded by every lane, read after the wait
-  bf16x8_t k[HD / 32]; // lanes lr == kl(p): K dims 32 i + 8 lg .. + 8
-  uint16_t v[HD / 16]; // lanes lg == p / 8: V dims 16 dt + lr
-};
-
-__device__ __forceinline__ int append_k_lane(int p) { return ((p >> 3) << 2) | (p & 3); }
-
+// Stream kernel: fetch for cursor c when it is its row's last group.
 template <int HD>
 __device__ __forceinline__ void append_load(Append<HD> &A, const DecodeArgs &a, const Cursor &c, int lr, int lg) {
-  constexpr int KS = HD / 32, DT = HD / 16;
   A.pending = a.slot_new != nullptr && c.j == c.ng - 1;
-  if (!A.pending) return;
-  A.p = c.n - 1 - c.j * kGroupPositions;
-  A.slot = a.slot_new[c.r];
-  const size_t base = ((size_t)c.r * a.n_kv_heads + c.kvh) * HD;
-  if (lr == append_k_lane(A.p)) {
-#pragma unroll
-    for (int i = 0; i < KS; ++i) A.k[i] = ld_bf16x8(a.k_new, (base + i * 32 + lg * 8) * 2);
-  }
-  if (lg == (A.p >> 3)) {
-    const uint16_t *vn = static_cast<const uint16_t *>(a.v_new) + base + lr;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) A.v[dt] = vn[dt * 16];
-  }
+  if (A.pending) append_fetch<HD>(A, a, c.r, c.kvh, c.n - 1 - c.j * kGroupPositions, lr, lg);
 }
 
-// After the group's tile has landed, before it is read.  The staging lane
-// layout: K tile tt row 8 (lr / 4) + 4 tt + lr % 4 holds dims 32 i + 8 lg in
-// slot (tt * KS + i) * 64 + lane; V slot dt * 64 + lane holds dim 16 dt + lr
-// at positions 8 lg .. 8 lg + 7.
+// Stream kernel: after the group's tile has landed in LDS, before it is read.
 template <int HD, int BS>
 __device__ __forceinline__ void append_apply(const Append<HD> &A, const DecodeArgs &a, const Cursor &c, uint4 *s_k,
                                              uint4 *s_v, int lane, int lr, int lg) {
   constexpr int KS = HD / 32, DT = HD / 16;
-  constexpr int LOG2_BS = BS == 8 ? 3 : (BS == 16 ? 4 : 5);
-  const int64_t s = (int64_t)(((uint64_t)(uint32_t)__builtin_amdgcn_readfirstlane((int)(A.slot >> 32)) << 32) |
-                              (uint32_t)__builtin_amdgcn_readfirstlane((int)A.slot));
-  if (s < 0 || s >= a.num_blocks * BS) return;
-  const int64_t blk = s >> LOG2_BS;
-  const int off = (int)(s & (BS - 1)), p = A.p;
+  const int64_t s = append_slot<BS>(A.slot, a);
+  if (s < 0) return;
+  append_store_pool<HD, BS>(A, a, c.kvh, s, lr, lg);
+  const int p = A.p;
   if (lr == append_k_lane(p)) {
     const int tt = (p >> 2) & 1;
-    uint16_t *kp = static_cast<uint16_t *>(const_cast<void *>(a.k_pool)) +
-                   ((((size_t)blk * a.n_kv_heads + c.kvh) << LOG2_BS) + off) * HD + lg * 8;
 #pragma unroll
-    for (int i = 0; i < KS; ++i) {
-      const uint4 x = __builtin_bit_cast(uint4, A.k[i]);
-      s_k[(tt * KS + i) * kWave + lane] = x;
-      *reinterpret_cast<uint4 *>(kp + i * 32) = x;
-    }
+    for (int i = 0; i < KS; ++i) s_k[(tt * KS + i) * kWave + lane] = __builtin_bit_cast(uint4, A.k[i]);
   }
   if (lg == (p >> 3)) {
-    uint16_t *vp = static_cast<uint16_t *>(const_cast<void *>(a.v_pool)) +
-                   ((((size_t)blk * a.n_kv_heads + c.kvh) * HD + lr) << LOG2_BS) + off;
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) {
-      reinterpret_cast<uint16_t *>(s_v + dt * kWave + lane)[p & 7] = A.v[dt];
-      vp[(size_t)dt * 16 * BS] = A.v[dt];
-    }
+    for (int dt = 0; dt < DT; ++dt) reinterpret_cast<uint16_t *>(s_v + dt * kWave + lane)[p & 7] = A.v[dt];
   }
 }
 

@@ -319,19 +319,22 @@ def equal_nan(a, b):
     return torch.equal(torch.isnan(a), torch.isnan(b)) and torch.equal(a.nan_to_num(0.0), b.nan_to_num(0.0))
 
 
-@pytest.mark.parametrize("rows,bs,prompt,hd", [
-    (32, 16, 200, 128),  # 256 (row, kv head) pairs, short table: partition kernel after a scatter
-    (64, 16, 200, 128),  # stream kernel appending the tokens itself: positions 8.. of a group
-    (64, 8, 29, 128),    # new tokens at the last position of a group, then the first ones
-    (40, 32, 61, 64),    # head_dim 64
-    (300, 16, 45, 128),  # more rows than a wave plans for: the plan kernel runs first
+@pytest.mark.parametrize("rows,bs,prompt,hd,dtype", [
+    (32, 16, 200, 128, "bf16"),  # 256 (row, kv head) pairs, short table: the partition kernel appends
+    (12, 8, 29, 64, "bf16"),     # partition kernel, head_dim 64, tokens crossing a group boundary
+    (64, 16, 200, 128, "bf16"),  # the stream kernel appends: positions 8.. of a group
+    (64, 8, 29, 128, "bf16"),    # new tokens at the last position of a group, then the first ones
+    (40, 32, 61, 64, "bf16"),    # head_dim 64
+    (300, 16, 45, 128, "bf16"),  # more rows than a wave plans for: the plan kernel runs first
+    (16, 16, 70, 16, "bf16"),    # head_dim 16: a scatter, then the VALU partition kernel
+    (16, 16, 70, 64, "f32"),     # fp32: a scatter, then the VALU partition kernel
 ])
-def test_decode_step_equals_scatter_then_read(rows, bs, prompt, hd):
+def test_decode_step_equals_scatter_then_read(rows, bs, prompt, hd, dtype):
     # bitwise: the one-call step (fused or not) against a scatter then a read.
     # Every third step some rows bring no token (slot -1): they read what the
     # pool holds, both ways.
-    run = synth.DecodeRun(rows=rows, block_size=bs, prompt=prompt, steps=6, head_dim=hd, device=DEV,
-                          seed=21 + rows + bs)
+    run = synth.DecodeRun(rows=rows, block_size=bs, prompt=prompt, steps=6, head_dim=hd, dtype=dtype,
+                          device=DEV, seed=21 + rows + bs)
     k, v, slots = run.prefill()
     pkv.reshape_and_cache(k, v, slots, run.k_pool, run.v_pool)
     kp2, vp2 = run.k_pool.clone(), run.v_pool.clone()
@@ -349,13 +352,14 @@ def test_decode_step_equals_scatter_then_read(rows, bs, prompt, hd):
         b = pkv.paged_attention(q, kp2, vp2, bt, cl, run.scale)
         torch.cuda.synchronize()
         assert equal_nan(a, b), "step %d" % step
-        assert torch.equal(run.k_pool.view(torch.int16), kp2.view(torch.int16))
-        assert torch.equal(run.v_pool.view(torch.int16), vp2.view(torch.int16))
+        word = torch.int16 if dtype == "bf16" else torch.int32
+        assert torch.equal(run.k_pool.view(word), kp2.view(word))
+        assert torch.equal(run.v_pool.view(word), vp2.view(word))
     # rows that never skipped a token read only what was written
     assert torch.isfinite(a.float().cpu()[~skipped]).all()
 
 
-@pytest.mark.parametrize("rows", [24, 48])  # scatter + partition kernel; stream kernel appending itself
+@pytest.mark.parametrize("rows", [24, 48])  # partition kernel, stream kernel: each appending the tokens itself
 def test_decode_step_replays_from_a_graph(rows):
     # capture once; every later step copies its inputs into the captured
     # tensors and replays.  Lengths grow and blocks are allocated between
