@@ -1207,6 +1207,7 @@ __device__ __forceinline__ void segment_end(const DecodeArgs &a, const StreamLay
 // rows in one slice were written by the stream kernel already.  The maxima
 // are read first (one independent load each), then the weighted sums.
 constexpr int kMergeMaxParts = 8;
+constexpr int kMergeElems = 2;
 __global__ __launch_bounds__(256) void decode_stream_merge(DecodeArgs a) {
   const StreamLayout L = stream_layout(a.rows, a.n_kv_heads, a.cols, a.head_dim, a.max_parts);
   const int32_t *wsi = reinterpret_cast<const int32_t *>(a.ws);
@@ -1255,40 +1256,60 @@ __global__ __launch_bounds__(256) void decode_stream_merge(DecodeArgs a) {
   if (nparts <= 1) return;
   const int C = a.cols, HD = a.head_dim;
   const float *slots = a.ws + L.partials + (size_t)pair * a.max_parts * L.slot_stride;
-  for (int idx = threadIdx.x; idx < C * HD; idx += blockDim.x) {
-    const int j = idx / HD, d = idx - j * HD;
-    float M = -INFINITY, Lm = 0.f, O = 0.f;
+  // Each thread merges kMergeElems outputs at a time, every partial load of
+  // them issued before any output is stored (a store in between would keep
+  // the next loads behind it: the compiler cannot tell out from the
+  // workspace).  Terms are taken in slice order.
+  for (int idx0 = threadIdx.x; idx0 < C * HD; idx0 += kMergeElems * blockDim.x) {
+    float M[kMergeElems], Lm[kMergeElems], O[kMergeElems];
+#pragma unroll
+    for (int e = 0; e < kMergeElems; ++e) M[e] = -INFINITY, Lm[e] = 0.f, O[e] = 0.f;
     for (int k0 = 0; k0 < nparts; k0 += kMergeMaxParts) {
       const int kn = min(nparts - k0, kMergeMaxParts);
-      float mk[kMergeMaxParts], lk[kMergeMaxParts], ak[kMergeMaxParts];
+      float mk[kMergeElems][kMergeMaxParts], lk[kMergeElems][kMergeMaxParts], ak[kMergeElems][kMergeMaxParts];
 #pragma unroll
-      for (int k = 0; k < kMergeMaxParts; ++k) {
-        if (k < kn) {
-          const float *sk = slots + (size_t)(k0 + k) * L.slot_stride;
-          mk[k] = sk[C * HD + j];
-          lk[k] = sk[C * HD + C + j];
-          ak[k] = sk[j * HD + d];
+      for (int e = 0; e < kMergeElems; ++e) {
+        const int idx = idx0 + e * blockDim.x;
+        const int j = idx / HD, d = idx - j * HD;
+#pragma unroll
+        for (int k = 0; k < kMergeMaxParts; ++k) {
+          if (idx < C * HD && k < kn) {
+            const float *sk = slots + (size_t)(k0 + k) * L.slot_stride;
+            mk[e][k] = sk[C * HD + j];
+            lk[e][k] = sk[C * HD + C + j];
+            ak[e][k] = sk[j * HD + d];
+          }
         }
       }
-      float mn = M;
 #pragma unroll
-      for (int k = 0; k < kMergeMaxParts; ++k)
-        if (k < kn) mn = fmaxf(mn, mk[k]);
-      const float a0 = M == -INFINITY ? 0.f : exp2_fast(M - mn);
-      Lm *= a0;
-      O *= a0;
+      for (int e = 0; e < kMergeElems; ++e) {
+        float mn = M[e];
 #pragma unroll
-      for (int k = 0; k < kMergeMaxParts; ++k) {
-        if (k < kn) {
-          // a slice that saw nothing of this column (m = -inf) adds nothing
-          const float wk = mk[k] == -INFINITY ? 0.f : exp2_fast(mk[k] - mn);
-          Lm = fmaf(lk[k], wk, Lm);
-          O = fmaf(ak[k], wk, O);
+        for (int k = 0; k < kMergeMaxParts; ++k)
+          if (k < kn) mn = fmaxf(mn, mk[e][k]);
+        const float a0 = M[e] == -INFINITY ? 0.f : exp2_fast(M[e] - mn);
+        Lm[e] *= a0;
+        O[e] *= a0;
+#pragma unroll
+        for (int k = 0; k < kMergeMaxParts; ++k) {
+          if (k < kn) {
+            // a slice that saw nothing of this column (m = -inf) adds nothing
+            const float wk = mk[e][k] == -INFINITY ? 0.f : exp2_fast(mk[e][k] - mn);
+            Lm[e] = fmaf(lk[e][k], wk, Lm[e]);
+            O[e] = fmaf(ak[e][k], wk, O[e]);
+          }
         }
+        M[e] = mn;
       }
-      M = mn;
     }
-    store_out(a.out, a.out_dtype, stream_out_row(a, kvh, r, j) * HD + d, Lm > 0.f ? O / Lm : 0.f);
+#pragma unroll
+    for (int e = 0; e < kMergeElems; ++e) {
+      const int idx = idx0 + e * blockDim.x;
+      if (idx < C * HD) {
+        const int j = idx / HD, d = idx - j * HD;
+        store_out(a.out, a.out_dtype, stream_out_row(a, kvh, r, j) * HD + d, Lm[e] > 0.f ? O[e] / Lm[e] : 0.f);
+      }
+    }
   }
 }
 

@@ -342,10 +342,12 @@ def test_decode_step_equals_scatter_then_read(rows, bs, prompt, hd, dtype):
     skipped = torch.zeros(rows, dtype=torch.bool)
     for step in range(run.steps):
         q, kn, vn, sl = run.step()
-        if step % 3 == 2:
+        if step % 3 == 2:  # no token (slot -1), or a slot past the pool: skipped both ways
             sl = sl.clone()
             sl[step::5] = -1
+            sl[step + 1::7] = run.num_blocks * bs
             skipped[step::5] = True
+            skipped[step + 1::7] = True
         bt, cl = run.block_table(), run.context_lens()
         a = pkv.decode_step(q, kn, vn, sl, run.k_pool, run.v_pool, bt, cl, run.scale)
         pkv.reshape_and_cache(kn, vn, sl, kp2, vp2)
