@@ -822,15 +822,15 @@ hipError_t launch_mfma(const DecodeArgs &a, hipStream_t stream) {
 //
 // The unit of work is a group of 32 consecutive positions of one (kv head,
 // row).  All groups, ordered by kv head, then row, then position, form one
-// stream; a tiny plan kernel prefix-sums the groups per row on the device
-// (no host sync) and cuts the stream into kStreamWaves equal contiguous
-// slices.  Each persistent wave walks its slice with the next group's K/V
+// stream, prefix-summed per row on the device (no host sync: inside every
+// wave for batches of at most kWindowRows rows, else by a plan kernel) and
+// cut into kStreamWaves equal contiguous slices.  Each persistent wave walks its slice with the next group's K/V
 // and the group after next's block ids in flight, across row boundaries, so
 // no wave waits on a partition start-up and every wave does the same work
 // whatever the length mix.  A (kv head, row) covered by one wave is written
 // to `out` directly; one cut into several slices gets one partial (max, sum,
-// rescaled acc) per slice, and the wave that writes the last partial (a
-// per-row counter, zeroed by the plan kernel on every call) merges them.
+// rescaled acc) per slice, which decode_stream_merge, the next kernel on
+// the stream, combines.
 // ---------------------------------------------------------------------------
 // Slice w of a stream of `total` groups cut into `waves` slices.
 __device__ __forceinline__ long long slice_start(long long w, long long total, long long waves) {
@@ -886,8 +886,6 @@ __global__ __launch_bounds__(1024) void decode_plan(DecodeArgs a) {
   if (tid == 0) {
     wsi[L.hdr] = ngk;
     wsi[L.hdr + 1] = (int)waves;
-    wsi[L.hdr + 2] = 0;
-    wsi[L.hdr + 3] = 0;
   }
   for (int r = tid; r <= rows; r += 1024) wsi[L.gpre + r] = s_gpre[r];
   const int pairs = a.n_kv_heads * rows;
@@ -1038,43 +1036,6 @@ __device__ __forceinline__ GroupIds load_ids(const DecodeArgs &a, const Cursor &
   ids.k1 = row[tk1 >> LOG2_BS];
   ids.v = row[tv >> LOG2_BS];
   return ids;
-}
-
-template <int HD, int BS>
-__device__ __forceinline__ void load_group_k(bf16x8_t (&k)[2][HD / 32], const DecodeArgs &a, const Cursor &c,
-                                             const GroupIds &ids, int lr, int lg) {
-  constexpr int KS = HD / 32;
-  constexpr int LOG2_BS = BS == 8 ? 3 : (BS == 16 ? 4 : 5);
-  constexpr int bmask = BS - 1;
-  const int t0 = c.j * kGroupPositions, last = c.n - 1;
-  const int64_t nb1 = a.num_blocks - 1;
-#pragma unroll
-  for (int tt = 0; tt < 2; ++tt) {
-    const int t = min(t0 + 8 * (lr >> 2) + 4 * tt + (lr & 3), last);
-    int64_t blk = tt == 0 ? ids.k0 : ids.k1;
-    blk = blk < 0 ? 0 : (blk > nb1 ? nb1 : blk);
-    const size_t row = (((size_t)blk * a.n_kv_heads + c.kvh) << LOG2_BS) + (t & bmask);
-    const char *kp = static_cast<const char *>(a.k_pool) + (row * HD + lg * 8) * 2;
-#pragma unroll
-    for (int i = 0; i < KS; ++i) k[tt][i] = ld_bf16x8(kp, i * 64);
-  }
-}
-
-template <int HD, int BS>
-__device__ __forceinline__ void load_group_v(bf16x8_t (&v)[HD / 16], const DecodeArgs &a, const Cursor &c,
-                                             const GroupIds &ids, int lr, int lg) {
-  constexpr int DT = HD / 16;
-  constexpr int LOG2_BS = BS == 8 ? 3 : (BS == 16 ? 4 : 5);
-  constexpr int bmask = BS - 1;
-  const int t0 = c.j * kGroupPositions, last = c.n - 1;
-  const int64_t nb1 = a.num_blocks - 1;
-  const int tv = min(t0 + 8 * lg, last) & ~7;
-  int64_t blk = ids.v;
-  blk = blk < 0 ? 0 : (blk > nb1 ? nb1 : blk);
-  const size_t base = ((((size_t)blk * a.n_kv_heads + c.kvh) * HD + lr) << LOG2_BS) + (tv & bmask);
-  const char *vp = static_cast<const char *>(a.v_pool) + base * 2;
-#pragma unroll
-  for (int dt = 0; dt < DT; ++dt) v[dt] = ld_bf16x8(vp, dt * 16 * BS * 2);
 }
 
 // Scores of one group: two 16x16 tiles (see the P.V layout note above).

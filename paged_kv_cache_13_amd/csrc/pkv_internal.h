@@ -68,17 +68,19 @@ __host__ __device__ inline WsLayout ws_layout(int32_t rows, int32_t n_heads, int
 // Stream decomposition of the bf16 read: the groups of 32 positions of all
 // (kv head, row) pairs, in that order, are cut into kStreamWaves equal
 // contiguous slices, one per persistent wave.  Workspace, in 4-byte words:
-//   hdr[4]                 groups per kv head, groups per wave, waves used
+//   hdr[4]                 groups per kv head, waves used, two words unused
 //   first_pos[2 * waves]   (kv head * rows + row, group) where each wave starts
 //   gpre[rows + 1]         exclusive prefix of groups per row
-//   counters[kv * rows]    partial slices written per (kv head, row)
 //   partials[kv * rows * max_parts][slot]  fp32 acc[cols][hd], m[cols], l[cols]
+// The plan words (hdr, first_pos, gpre) are written by decode_plan; a batch
+// of at most kWindowRows rows is planned inside every wave and leaves them
+// unused.
 constexpr int kStreamWaves = 1024;  // one persistent wave per SIMD (4 per CU)
 constexpr int kWindowRows = 256;  // rows a wave keeps (and, if that is all, plans) in LDS
 constexpr int kPlanMaxRows = 8192;
 constexpr int kGroupPositions = 32;
 struct StreamLayout {
-  size_t hdr, first_pos, gpre, counters, partials, total;
+  size_t hdr, first_pos, gpre, partials, total;
   size_t slot_stride;
 };
 __host__ __device__ inline size_t align4(size_t x) { return (x + 3) & ~(size_t)3; }
@@ -88,8 +90,7 @@ __host__ __device__ inline StreamLayout stream_layout(int32_t rows, int32_t n_kv
   L.hdr = 0;
   L.first_pos = 4;
   L.gpre = L.first_pos + 2 * (size_t)kStreamWaves;
-  L.counters = L.gpre + (size_t)rows + 1;
-  L.partials = align4(L.counters + (size_t)n_kv * rows);
+  L.partials = align4(L.gpre + (size_t)rows + 1);
   L.slot_stride = align4((size_t)cols * (head_dim + 2));
   L.total = L.partials + (size_t)n_kv * rows * max_parts * L.slot_stride;
   return L;

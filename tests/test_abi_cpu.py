@@ -85,11 +85,11 @@ def test_workspace_size_partition_layout(lib):
 
 def test_workspace_size_stream_layout(lib):
     # bf16, head_dim 128: header (4 words), 1024 wave starts (2 words each),
-    # 65 group prefixes, 8 x 64 row counters, aligned; then per (kv head, row)
+    # 65 group prefixes, aligned; then per (kv head, row)
     # one partial slot of align4(4 heads x 130) = 520 floats per slice that can
     # cut it: the default slices hold at least 4 groups of 32 positions, so
     # 128 / 4 + 1 = 33 slots
-    head = 4 + 2 * 1024 + 65 + 8 * 64
+    head = 4 + 2 * 1024 + 65
     head += -head % 4
     assert ws(lib) == (head + 8 * 64 * 33 * 520) * 4
     # an explicit partition length sets the minimum slice: 512 -> 16 groups
@@ -262,10 +262,10 @@ def test_multi_query_workspace(lib):
     ws = lambda d, q: lib.pkv_paged_attention_multi_workspace_size(ctypes.byref(d), q)
     # 4 queries x 4 heads per kv head = 16 columns: the stream path, whose
     # workspace is the one-query read's layout with 16 columns per slot --
-    # header, wave starts, row prefixes, counters, then 33 slices (4-group
+    # header, wave starts, row prefixes, then 33 slices (4-group
     # minimum over a 128-group table) per (kv head, row) of 16 x (128 + 2)
     d = desc()
-    head = 4 + 2 * 1024 + 65 + 8 * 64
+    head = 4 + 2 * 1024 + 65
     head = (head + 3) & ~3
     assert ws(d, 4) == (head + 8 * 64 * 33 * 16 * 130) * 4
     # 8 queries (32 columns): the workgroup path.  64 rows x 8 kv heads x one
