@@ -204,11 +204,10 @@ size_t pkv_paged_attention_multi_workspace_size(const pkv_attn_desc *d, int32_t 
  * after every check of both has passed (a refused call enqueues nothing).
  * The new token of row r is counted in context_lens[r] and lives at
  * slot_mapping[r]: it is position context_lens[r] - 1 of the row.  The
- * bf16 reads with head_dim 64 or 128 append the tokens themselves (the wave
- * or workgroup that reads a row's last position stores the row's token
- * first), so the step is one read launch; fp32 and head_dim 16 reads run
- * after a scatter kernel.  Results and pools are bit for bit those of the
- * two calls.  The kernels' launch shapes depend on the descriptor
+ * read kernels append the tokens themselves (the wave or workgroup that
+ * reads a row's last position stores the row's token first), so the step is
+ * one read launch.  Results and pools are bit for bit those of the two
+ * calls.  The kernels' launch shapes depend on the descriptor
  * only (rows, heads, head_dim, block size, table width), never on lengths or
  * block ids, so a captured graph of this call replays for any lengths.
  *

@@ -277,8 +277,8 @@ def decode_step(q, k_new, v_new, slot_mapping, k_pool, v_pool, block_table, cont
                 stats: Optional["ReadCounters"] = None) -> torch.Tensor:
     """One decode step of every row: scatter k_new, v_new [rows, n_kv, hd] to
     slot_mapping [rows] (int64), then the paged read of q -- one library call
-    on the current stream, no host synchronisation.  bf16 reads with head_dim
-    64 / 128 append the new tokens themselves; the others run after a scatter."""
+    on the current stream, no host synchronisation.  The read kernels append
+    the new tokens themselves: one read launch per step."""
     if out is None:
         out = torch.empty_like(q)
     dev, d, wsp, wsb = _read_args(q, k_pool, v_pool, block_table, context_lens, out, workspace,

@@ -421,16 +421,10 @@ int pkv_decode_step(const pkv_attn_desc *d, const void *k_new, const void *v_new
   if (st != PKV_OK) return st;
   if (d->rows == 0) return PKV_OK;
   const hipStream_t hs = static_cast<hipStream_t>(stream);
-  // The bf16 reads with head_dim 64 / 128 (stream and partition kernels)
-  // append the new tokens themselves (one launch less); the other read
-  // kernels run after a scatter.
-  if (d->dtype == PKV_BF16 && (d->head_dim == 64 || d->head_dim == 128))
-    return launch_attention(d, pl, q, k_pool, v_pool, block_table, context_lens, scale, out, workspace, hs,
-                            k_new, v_new, slot_mapping);
-  if (pkv::launch_scatter(k_new, v_new, slot_mapping, d->rows, k_pool, v_pool, d->num_blocks,
-                          d->block_size, d->n_kv_heads, d->head_dim, d->dtype, hs) != hipSuccess)
-    return PKV_ERR_LAUNCH;
-  return launch_attention(d, pl, q, k_pool, v_pool, block_table, context_lens, scale, out, workspace, hs);
+  // Every read kernel appends the new tokens itself: one launch less than a
+  // scatter followed by a read.
+  return launch_attention(d, pl, q, k_pool, v_pool, block_table, context_lens, scale, out, workspace, hs,
+                          k_new, v_new, slot_mapping);
 }
 
 int pkv_read_stats_init(pkv_read_stats *s, int32_t mode, int32_t block) {

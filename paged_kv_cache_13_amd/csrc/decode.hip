@@ -194,6 +194,34 @@ __device__ __forceinline__ WorkItem work_item(const DecodeArgs &a) {
   return w;
 }
 
+// Partition kernels: one kv head's new token of row r, stored into its pool
+// slot by threads t0, t0 + nthreads, ... (skipped like the scatter skips).
+// E: the pool's element type, bit-copied.
+template <typename E>
+__device__ __forceinline__ void append_store_row(const DecodeArgs &a, int r, int kvh, int t0, int nthreads) {
+  const int64_t s = a.slot_new[r];
+  if (s < 0 || s >= a.num_blocks * a.block_size) return;
+  const int64_t blk = s >> a.log2_bs, off = s & (a.block_size - 1);
+  const size_t src = ((size_t)r * a.n_kv_heads + kvh) * a.head_dim;
+  const E *kn = static_cast<const E *>(a.k_new) + src;
+  const E *vn = static_cast<const E *>(a.v_new) + src;
+  E *kp = static_cast<E *>(const_cast<void *>(a.k_pool)) +
+          ((((size_t)blk * a.n_kv_heads + kvh) << a.log2_bs) + off) * a.head_dim;
+  E *vp = static_cast<E *>(const_cast<void *>(a.v_pool)) +
+          ((((size_t)blk * a.n_kv_heads + kvh) * a.head_dim) << a.log2_bs) + off;
+  for (int d = t0; d < a.head_dim; d += nthreads) {
+    kp[d] = kn[d];
+    vp[(size_t)d << a.log2_bs] = vn[d];
+  }
+}
+
+// A row with no positions that still brings a token: appended whole (every
+// kv head) by the threads that zero-fill the row, as the scatter would.
+template <typename E>
+__device__ __forceinline__ void append_empty_row(const DecodeArgs &a, int r, int t0, int nthreads) {
+  for (int h = 0; h < a.n_kv_heads; ++h) append_store_row<E>(a, r, h, t0, nthreads);
+}
+
 template <typename T, int HD, int GP>
 __global__ __launch_bounds__(kThreads) void decode_partition(DecodeArgs a) {
   constexpr int ES = sizeof(T);
@@ -223,6 +251,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition(DecodeArgs a) {
         const int j = idx / HD, d = idx % HD;
         store_out(a.out, a.out_dtype, ((size_t)r * a.n_heads + g * group + j) * HD + d, 0.f);
       }
+      if (n == 0 && g == 0 && a.slot_new) append_empty_row<T>(a, r, tid, kThreads);
     }
     return;
   }
@@ -253,6 +282,14 @@ __global__ __launch_bounds__(kThreads) void decode_partition(DecodeArgs a) {
     else
       qv[j] = make_uint4(0, 0, 0, 0);
   }
+  // A decode step's new token (position n - 1) in this partition: stored
+  // into its pool slot before any K/V is loaded, as in the MFMA partition
+  // kernel.
+  if (a.slot_new != nullptr && n - 1 < end) {
+    append_store_row<T>(a, r, g, tid, kThreads);
+    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores have completed
+  }
+  __threadfence_block();
   __syncthreads();
 
   const float sl2 = a.scale * kLog2e;
@@ -635,43 +672,6 @@ __device__ __forceinline__ void append_store_pool(const Append<HD> &A, const Dec
   }
 }
 
-// Partition kernel: one kv head's new token of row r, stored into its pool
-// slot by threads t0, t0 + nthreads, ... (skipped like the scatter skips).
-__device__ __forceinline__ void append_store_row(const DecodeArgs &a, int r, int kvh, int t0, int nthreads) {
-  const int64_t s = a.slot_new[r];
-  if (s < 0 || s >= a.num_blocks * a.block_size) return;
-  const int64_t blk = s >> a.log2_bs, off = s & (a.block_size - 1);
-  const size_t src = ((size_t)r * a.n_kv_heads + kvh) * a.head_dim;
-  const uint16_t *kn = static_cast<const uint16_t *>(a.k_new) + src;
-  const uint16_t *vn = static_cast<const uint16_t *>(a.v_new) + src;
-  uint16_t *kp = static_cast<uint16_t *>(const_cast<void *>(a.k_pool)) +
-                 ((((size_t)blk * a.n_kv_heads + kvh) << a.log2_bs) + off) * a.head_dim;
-  uint16_t *vp = static_cast<uint16_t *>(const_cast<void *>(a.v_pool)) +
-                 ((((size_t)blk * a.n_kv_heads + kvh) * a.head_dim) << a.log2_bs) + off;
-  for (int d = t0; d < a.head_dim; d += nthreads) {
-    kp[d] = kn[d];
-    vp[(size_t)d << a.log2_bs] = vn[d];
-  }
-}
-
-// A row with no positions that still brings a token: appended whole (every
-// kv head) by the wave that zero-fills the row, as the scatter would.
-__device__ __forceinline__ void append_empty_row(const DecodeArgs &a, int r, int t0, int nthreads) {
-  const int64_t s = a.slot_new[r];
-  if (s < 0 || s >= a.num_blocks * a.block_size) return;
-  const int64_t blk = s >> a.log2_bs, off = s & (a.block_size - 1);
-  const int per = a.n_kv_heads * a.head_dim;
-  const uint16_t *kn = static_cast<const uint16_t *>(a.k_new) + (size_t)r * per;
-  const uint16_t *vn = static_cast<const uint16_t *>(a.v_new) + (size_t)r * per;
-  uint16_t *kp = static_cast<uint16_t *>(const_cast<void *>(a.k_pool));
-  uint16_t *vp = static_cast<uint16_t *>(const_cast<void *>(a.v_pool));
-  for (int e = t0; e < per; e += nthreads) {
-    const int h = e / a.head_dim, d = e - h * a.head_dim;
-    kp[((((size_t)blk * a.n_kv_heads + h) << a.log2_bs) + off) * a.head_dim + d] = kn[e];
-    vp[((((size_t)blk * a.n_kv_heads + h) * a.head_dim + d) << a.log2_bs) + off] = vn[e];
-  }
-}
-
 template <int HD, int BS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_partition_mfma(DecodeArgs a) {
   constexpr int KS = HD / 32, DT = HD / 16, GT = 32;
@@ -695,7 +695,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         const int j = idx / HD, d = idx % HD;
         store_out(a.out, a.out_dtype, ((size_t)r * a.n_heads + g * group + j) * HD + d, 0.f);
       }
-      if (n == 0 && g == 0 && a.slot_new) append_empty_row(a, r, tid, kThreads);
+      if (n == 0 && g == 0 && a.slot_new) append_empty_row<uint16_t>(a, r, tid, kThreads);
     }
     return;
   }
@@ -727,7 +727,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // the pool like any other position: the same bits as a scatter followed
   // by a read.
   if (a.slot_new != nullptr && n - 1 < end) {
-    append_store_row(a, r, g, tid, kThreads);
+    append_store_row<uint16_t>(a, r, g, tid, kThreads);
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores have completed
   }
   __threadfence_block();
@@ -860,7 +860,7 @@ __global__ __launch_bounds__(1024) void decode_plan(DecodeArgs a) {
     if (n == 0) {  // an empty row reads zeros (all its queries); no wave visits it
       const size_t per_row = (size_t)a.query_len * a.n_heads * a.head_dim;
       for (size_t idx = 0; idx < per_row; ++idx) store_out(a.out, a.out_dtype, (size_t)r * per_row + idx, 0.f);
-      if (a.slot_new) append_empty_row(a, r, 0, 1);
+      if (a.slot_new) append_empty_row<uint16_t>(a, r, 0, 1);
     }
   }
   s_sum[tid] = local;
@@ -1376,7 +1376,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
       const int per_row = a.query_len * a.n_heads * a.head_dim;
       for (int idx = lane; idx < per_row; idx += kWave)
         store_out(a.out, a.out_dtype, (size_t)w * per_row + idx, 0.f);
-      if (a.slot_new) append_empty_row(a, w, lane, kWave);
+      if (a.slot_new) append_empty_row<uint16_t>(a, w, lane, kWave);
     }
     if (ng_all0 == 0 || w >= waves) return;
     const long long st = slice_start(w, ng_all0, waves);

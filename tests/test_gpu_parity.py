@@ -326,11 +326,12 @@ def equal_nan(a, b):
     (64, 8, 29, 128, "bf16"),    # new tokens at the last position of a group, then the first ones
     (40, 32, 61, 64, "bf16"),    # head_dim 64
     (300, 16, 45, 128, "bf16"),  # more rows than a wave plans for: the plan kernel runs first
-    (16, 16, 70, 16, "bf16"),    # head_dim 16: a scatter, then the VALU partition kernel
-    (16, 16, 70, 64, "f32"),     # fp32: a scatter, then the VALU partition kernel
+    (16, 16, 70, 16, "bf16"),    # head_dim 16: the VALU partition kernel appends
+    (16, 16, 70, 64, "f32"),     # fp32: the VALU partition kernel appends
 ])
 def test_decode_step_equals_scatter_then_read(rows, bs, prompt, hd, dtype):
-    # bitwise: the one-call step (fused or not) against a scatter then a read.
+    # bitwise: the one-call step, whose read appends the tokens itself,
+    # against a scatter then a read.
     # Every third step some rows bring no token (slot -1): they read what the
     # pool holds, both ways.
     run = synth.DecodeRun(rows=rows, block_size=bs, prompt=prompt, steps=6, head_dim=hd, dtype=dtype,
