@@ -51,6 +51,27 @@ int32_t default_partition(const pkv_attn_desc *d, int32_t cap) {
   return (int32_t)part;
 }
 
+// Default partition of the MFMA partition kernel (bf16, head_dim 64/128: small
+// batches over short tables, and batches too large for the stream plan): as
+// few partitions as give one workgroup per compute unit, none shorter than
+// kMfmaMinPartition positions unless the table is -- a split costs a merge
+// launch, worth about six 32-position groups per wave -- and none longer
+// than kMfmaMaxPartition, so that a long row is still cut.  Measured on the
+// 8B-shaped layer (us, default before / after): 32 rows x 768 positions 22.5
+// / 19.2, 16 x 768 15.6 / 13.5, 8 x 2048 19.9 / 18.3, 32 x 2048 43.8 / 39.2,
+// 16 x 4096 43.6 / 40.0 (4096-position partitions: 44.2).
+constexpr int64_t kMfmaTargetWorkgroups = 256;
+constexpr int32_t kMfmaMinPartition = 768;
+constexpr int32_t kMfmaMaxPartition = 2048;
+int32_t default_partition_mfma(const pkv_attn_desc *d, int32_t cap) {
+  const int64_t pairs = (int64_t)d->n_kv_heads * (d->rows > 0 ? d->rows : 1);
+  const int64_t want_parts = (kMfmaTargetWorkgroups + pairs - 1) / pairs;
+  int64_t part = (cap + want_parts - 1) / want_parts;
+  part = std::min<int64_t>(std::max<int64_t>(part, kMfmaMinPartition), kMfmaMaxPartition);
+  part = (part + d->block_size - 1) / d->block_size * d->block_size;
+  return (int32_t)part;
+}
+
 constexpr int64_t kSmallBatchPairs = 256;   // (kv head, row) pairs
 constexpr int64_t kSmallBatchTable = 4096;  // positions a row's table can hold
 struct Plan {
@@ -73,15 +94,6 @@ int plan_decode(const pkv_attn_desc *d, Plan *pl) {
       !pool_fits(d->num_blocks, d->block_size, d->n_kv_heads, d->head_dim, d->dtype))
     return PKV_ERR_SHAPE;
   const int32_t cap = d->max_blocks_per_row * d->block_size;
-  int32_t part = d->partition_tokens;
-  if (part == 0) part = default_partition(d, cap);
-  if (part < 0 || part % d->block_size != 0) return PKV_ERR_PARTITION;
-  if (part > cap) part = cap;  // one partition covers every row: no split
-  if (part / d->block_size > kMaxPartitionBlocks) return PKV_ERR_PARTITION;
-  pl->group = d->n_heads / d->n_kv_heads;
-  pl->partition = part;
-  pl->log2_bs = log2i(d->block_size);
-  pl->ws_bytes = 0;
   // bf16 with head_dim 64/128 runs the balanced stream decomposition when the
   // plan kernel can hold the rows and the group count fits in 31 bits;
   // everything else runs one workgroup per (partition, kv head, row).  So
@@ -91,9 +103,18 @@ int plan_decode(const pkv_attn_desc *d, Plan *pl) {
   // tables keep the stream's balance (4 rows x 32k positions: 100 vs 128 us).
   const int64_t cap_groups = (cap + pkv::kGroupPositions - 1) / pkv::kGroupPositions;
   const bool small_batch = (int64_t)d->rows * d->n_kv_heads <= kSmallBatchPairs && cap <= kSmallBatchTable;
-  pl->stream = d->dtype == PKV_BF16 && (d->head_dim == 64 || d->head_dim == 128) &&
-               d->rows <= pkv::kPlanMaxRows && !small_batch &&
+  const bool mfma = d->dtype == PKV_BF16 && (d->head_dim == 64 || d->head_dim == 128);
+  pl->stream = mfma && d->rows <= pkv::kPlanMaxRows && !small_batch &&
                cap_groups * d->n_kv_heads * d->rows < (int64_t)INT_MAX;
+  int32_t part = d->partition_tokens;
+  if (part == 0) part = mfma && !pl->stream ? default_partition_mfma(d, cap) : default_partition(d, cap);
+  if (part < 0 || part % d->block_size != 0) return PKV_ERR_PARTITION;
+  if (part > cap) part = cap;  // one partition covers every row: no split
+  if (part / d->block_size > kMaxPartitionBlocks) return PKV_ERR_PARTITION;
+  pl->group = d->n_heads / d->n_kv_heads;
+  pl->partition = part;
+  pl->log2_bs = log2i(d->block_size);
+  pl->ws_bytes = 0;
   if (pl->stream) {
     // slices of at least cg_min groups: the caller's partition length, else
     // kStreamMinGroups, short enough that a small batch still fills every wave

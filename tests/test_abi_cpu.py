@@ -102,10 +102,17 @@ def test_workspace_size_stream_layout(lib):
 
 def test_small_batches_over_short_tables_take_partitions(lib):
     # at most 256 (row, kv head) pairs over a table of at most 4096 positions:
-    # the bf16 read uses the partition layout, the same as an fp32 read
+    # the bf16 read uses the partition layout (that of an fp32 read with the
+    # same partition length).  Its default partition: one workgroup per
+    # compute unit (256 pairs: one partition), within [768, 2048] positions.
     part = lambda **kw: ws(lib, dtype=0, out_dtype=0, **kw)
-    assert ws(lib, rows=32) == part(rows=32)                      # 256 pairs, 4096 positions
-    assert ws(lib, rows=2, max_blocks_per_row=64) == part(rows=2, max_blocks_per_row=64)
+    assert ws(lib, rows=32) == part(rows=32, partition_tokens=2048)   # 4096 positions: two of 2048
+    assert ws(lib, rows=32) == (2 * 32 * 32 * 2 + 32 * 32 * 2 * 128) * 4
+    assert ws(lib, rows=32, max_blocks_per_row=48) == 0                # 768 positions: one partition
+    assert ws(lib, rows=8, max_blocks_per_row=128) == part(rows=8, max_blocks_per_row=128,
+                                                           partition_tokens=768)  # 64 pairs: 4 -> 768
+    assert ws(lib, rows=2, max_blocks_per_row=64) == part(rows=2, max_blocks_per_row=64,
+                                                          partition_tokens=768)  # 16 pairs: the floor
     # one more position, or one more row, and the stream layout comes back
     assert ws(lib, rows=32, max_blocks_per_row=257) != part(rows=32, max_blocks_per_row=257)
     assert ws(lib, rows=33) != part(rows=33)
