@@ -74,6 +74,7 @@ int32_t default_partition_mfma(const pkv_attn_desc *d, int32_t cap) {
 
 constexpr int64_t kSmallBatchPairs = 256;   // (kv head, row) pairs
 constexpr int64_t kSmallBatchTable = 4096;  // positions a row's table can hold
+constexpr int64_t kShortTable = 1024;       // positions: the partition kernel at any batch
 struct Plan {
   int32_t group, partition, max_parts, log2_bs;
   int32_t stream, cg_min;
@@ -97,12 +98,17 @@ int plan_decode(const pkv_attn_desc *d, Plan *pl) {
   // bf16 with head_dim 64/128 runs the balanced stream decomposition when the
   // plan kernel can hold the rows and the group count fits in 31 bits;
   // everything else runs one workgroup per (partition, kv head, row).  So
-  // does a small batch over a short table: there the partition kernel's one
-  // launch beats the stream's fixed start-up and merge (8B-shaped layer:
-  // 8 rows x 1k positions 17 vs 23 us, 32 rows x 4k 58 vs 61 us), while long
-  // tables keep the stream's balance (4 rows x 32k positions: 100 vs 128 us).
+  // does a table of at most kShortTable positions, and a small batch over a
+  // table of at most kSmallBatchTable: there the partition kernel, one
+  // launch with at most a few workgroups per row, beats the stream's fixed
+  // start-up and merge, while long tables keep the stream's balance.
+  // Measured on the 8B-shaped layer (us, stream / partition): 128 rows x 768
+  // positions 72.4 / 62.7, 96 x 1024 63.0 / 55.0, 32 x 4096 65.2 / 64.8;
+  // 64 x 2048 86.6 / 90.9, 48 x 4096 83.2 / 100.7, 64 x 4096 106 / 125,
+  // 32 x 8192 154 / 179, 4 x 32768 100 / 128.
   const int64_t cap_groups = (cap + pkv::kGroupPositions - 1) / pkv::kGroupPositions;
-  const bool small_batch = (int64_t)d->rows * d->n_kv_heads <= kSmallBatchPairs && cap <= kSmallBatchTable;
+  const bool small_batch = cap <= kShortTable ||
+                           ((int64_t)d->rows * d->n_kv_heads <= kSmallBatchPairs && cap <= kSmallBatchTable);
   const bool mfma = d->dtype == PKV_BF16 && (d->head_dim == 64 || d->head_dim == 128);
   pl->stream = mfma && d->rows <= pkv::kPlanMaxRows && !small_batch &&
                cap_groups * d->n_kv_heads * d->rows < (int64_t)INT_MAX;

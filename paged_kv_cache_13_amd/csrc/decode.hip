@@ -672,6 +672,52 @@ __device__ __forceinline__ void append_store_pool(const Append<HD> &A, const Dec
   }
 }
 
+// One kv head's new token of a row in one wave's registers: lane l holds K
+// and V dims l, l + 64, ... of the row (bf16), and the slot.
+template <int HD>
+struct TokenRow {
+  int64_t slot;
+  uint16_t k[(HD + kWave - 1) / kWave], v[(HD + kWave - 1) / kWave];
+};
+
+template <int HD>
+__device__ __forceinline__ void token_fetch(TokenRow<HD> &t, const DecodeArgs &a, int r, int kvh, int lane) {
+  constexpr int PER = (HD + kWave - 1) / kWave;
+  t.slot = a.slot_new[r];
+  const size_t src = ((size_t)r * a.n_kv_heads + kvh) * HD;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int d = lane + i * kWave;
+    if (d < HD) {
+      t.k[i] = static_cast<const uint16_t *>(a.k_new)[src + d];
+      t.v[i] = static_cast<const uint16_t *>(a.v_new)[src + d];
+    }
+  }
+}
+
+// The stores, skipped for slots the scatter would skip.
+template <int HD, int BS>
+__device__ __forceinline__ void token_store(const TokenRow<HD> &t, const DecodeArgs &a, int kvh, int lane) {
+  constexpr int PER = (HD + kWave - 1) / kWave;
+  constexpr int LOG2_BS = BS == 8 ? 3 : (BS == 16 ? 4 : 5);
+  const int64_t s = t.slot;
+  if (s < 0 || s >= a.num_blocks * BS) return;
+  const int64_t blk = s >> LOG2_BS;
+  const int off = (int)(s & (BS - 1));
+  uint16_t *kp = static_cast<uint16_t *>(const_cast<void *>(a.k_pool)) +
+                 ((((size_t)blk * a.n_kv_heads + kvh) << LOG2_BS) + off) * HD;
+  uint16_t *vp = static_cast<uint16_t *>(const_cast<void *>(a.v_pool)) +
+                 ((((size_t)blk * a.n_kv_heads + kvh) * HD) << LOG2_BS) + off;
+#pragma unroll
+  for (int i = 0; i < PER; ++i) {
+    const int d = lane + i * kWave;
+    if (d < HD) {
+      kp[d] = t.k[i];
+      vp[(size_t)d << LOG2_BS] = t.v[i];
+    }
+  }
+}
+
 template <int HD, int BS>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_partition_mfma(DecodeArgs a) {
   constexpr int KS = HD / 32, DT = HD / 16, GT = 32;
@@ -701,6 +747,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   }
   const int end = min(n, start + P);
   const bool single = n <= P;
+  const int lane = tid % kWave;
+  const int wave = tid / kWave;
+  const int lr = lane & 15;  // head of the group (N index)
+  const int lg = lane >> 4;  // k-slot group
+
+  // A decode step's new token (position n - 1) in this partition: the wave
+  // that loads its 32-position group stores it into its pool slot first, so
+  // its own later load of that group reads it back (one wave's accesses to
+  // an address stay in order); no other wave reads the slot.  Its K and V
+  // row come in with the block ids, and the stores add no wait.
+  const bool tok_wave = a.slot_new != nullptr && n - 1 < end && ((n - 1 - start) / GT) % kWaves == wave;
+  TokenRow<HD> tok;
+  if (tok_wave) token_fetch<HD>(tok, a, r, g, lane);
   const int nblk = (end - start + a.block_size - 1) >> a.log2_bs;
   const int32_t *table_row = a.block_table + (size_t)r * a.max_blocks_per_row + (start >> a.log2_bs);
   for (int i = tid; i < nblk; i += kThreads) {
@@ -709,28 +768,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     s_blk[i] = (int32_t)b;
   }
 
-  const int lane = tid % kWave;
-  const int wave = tid / kWave;
-  const int lr = lane & 15;  // head of the group (N index)
-  const int lg = lane >> 4;  // k-slot group
-
   bf16x8_t qb[KS];
 #pragma unroll
   for (int i = 0; i < KS; ++i)
     qb[i] = lr < group
                 ? ld_bf16x8(a.q, (((size_t)r * a.n_heads + g * group + lr) * HD + (4 * i + lg) * 8) * 2)
                 : zero_bf16x8();
-  // A decode step's new token (position n - 1) in this partition: stored
-  // into its pool slot before any K/V of the partition is loaded; the
-  // stores complete, and a workgroup-scope fence and the barrier order them
-  // before every wave's loads (the waves share one vector L1).  The loop then reads it from
-  // the pool like any other position: the same bits as a scatter followed
-  // by a read.
-  if (a.slot_new != nullptr && n - 1 < end) {
-    append_store_row<uint16_t>(a, r, g, tid, kThreads);
-    __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0): the stores have completed
-  }
-  __threadfence_block();
+  if (tok_wave) token_store<HD, BS>(tok, a, g, lane);
   __syncthreads();
 
   const float c = a.scale * kLog2e;

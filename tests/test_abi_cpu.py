@@ -113,6 +113,10 @@ def test_small_batches_over_short_tables_take_partitions(lib):
                                                            partition_tokens=768)  # 64 pairs: 4 -> 768
     assert ws(lib, rows=2, max_blocks_per_row=64) == part(rows=2, max_blocks_per_row=64,
                                                           partition_tokens=768)  # 16 pairs: the floor
+    # a table of at most 1024 positions takes the partition kernel at any batch
+    assert ws(lib, rows=128, max_blocks_per_row=64) == part(rows=128, max_blocks_per_row=64,
+                                                            partition_tokens=1024)  # one partition: 0
+    assert ws(lib, rows=128, max_blocks_per_row=65) > 4 * (2 * 1024)  # 1040 positions: stream header
     # one more position, or one more row, and the stream layout comes back
     assert ws(lib, rows=32, max_blocks_per_row=257) != part(rows=32, max_blocks_per_row=257)
     assert ws(lib, rows=33) != part(rows=33)

@@ -320,12 +320,12 @@ def equal_nan(a, b):
 
 
 @pytest.mark.parametrize("rows,bs,prompt,hd,dtype", [
-    (32, 16, 200, 128, "bf16"),  # 256 (row, kv head) pairs, short table: the partition kernel appends
-    (12, 8, 29, 64, "bf16"),     # partition kernel, head_dim 64, tokens crossing a group boundary
-    (64, 16, 200, 128, "bf16"),  # the stream kernel appends: positions 8.. of a group
-    (64, 8, 29, 128, "bf16"),    # new tokens at the last position of a group, then the first ones
-    (40, 32, 61, 64, "bf16"),    # head_dim 64
-    (300, 16, 45, 128, "bf16"),  # more rows than a wave plans for: the plan kernel runs first
+    (32, 16, 200, 128, "bf16"),   # short table: the partition kernel appends
+    (12, 8, 29, 64, "bf16"),      # partition kernel, head_dim 64, tokens crossing a group boundary
+    (64, 16, 1100, 128, "bf16"),  # tables over 1024 positions: the stream kernel appends (positions 12..)
+    (64, 8, 1053, 128, "bf16"),   # new tokens at the last positions of a group, then the first ones
+    (40, 32, 1085, 64, "bf16"),   # head_dim 64
+    (300, 16, 1040, 128, "bf16"),  # more rows than a wave plans for: the plan kernel runs first
     (16, 16, 70, 16, "bf16"),    # head_dim 16: the VALU partition kernel appends
     (16, 16, 70, 64, "f32"),     # fp32: the VALU partition kernel appends
 ])
@@ -362,14 +362,15 @@ def test_decode_step_equals_scatter_then_read(rows, bs, prompt, hd, dtype):
     assert torch.isfinite(a.float().cpu()[~skipped]).all()
 
 
-@pytest.mark.parametrize("rows", [24, 48])  # partition kernel, stream kernel: each appending the tokens itself
-def test_decode_step_replays_from_a_graph(rows):
+@pytest.mark.parametrize("rows,prompt", [(24, 120), (48, 1100)])  # partition kernel, stream kernel
+def test_decode_step_replays_from_a_graph(rows, prompt):
     # capture once; every later step copies its inputs into the captured
     # tensors and replays.  Lengths grow and blocks are allocated between
     # replays, the launch shape stays rows-only.  Each replay is checked
     # against the same step run eagerly on a second copy of the pools.
+    # Either kernel appends the tokens itself.
     bs = 16
-    run = synth.DecodeRun(rows=rows, block_size=bs, prompt=120, steps=24, device=DEV, seed=22)
+    run = synth.DecodeRun(rows=rows, block_size=bs, prompt=prompt, steps=24, device=DEV, seed=22)
     k, v, slots = run.prefill()
     pkv.reshape_and_cache(k, v, slots, run.k_pool, run.v_pool)
     kp_ref, vp_ref = run.k_pool.clone(), run.v_pool.clone()
@@ -465,14 +466,17 @@ def test_read_edge_lengths_bf16(bs, hd, width):
         assert np.array_equal(got[8], np.zeros_like(got[8]))
 
 
+@pytest.mark.parametrize("width", [704, 1056])
 @pytest.mark.parametrize("rows", [257, 600])
-def test_read_many_rows(rows):
-    # more rows than a wave plans for itself: the plan kernel path
+def test_read_many_rows(rows, width):
+    # more rows than a wave plans for itself.  A table of at most 1024
+    # positions is read by the partition kernel; a wider one by the stream
+    # kernels, after the plan kernel.
     lens = np.random.default_rng(rows).integers(0, 701, size=rows)
     lens[::37] = 0  # some empty rows
     cfg = synth.DecodeConfig("many", "bf16", rows=rows, n_heads=32, n_kv_heads=8, head_dim=128,
                              block_size=16, ctx=("fixed", tuple(int(x) for x in lens)),
-                             pool=("factor", 1.5), max_ctx=704, seed=rows)
+                             pool=("factor", 1.5), max_ctx=width, seed=rows)
     b = synth.make_batch(cfg, device=DEV)
     sample = np.unique(np.concatenate([np.arange(6), np.arange(rows - 6, rows), [37, 74],
                                        np.random.default_rng(1).choice(rows, 12, replace=False)]))
