@@ -37,10 +37,11 @@ bool pool_fits(int64_t num_blocks, int32_t bs, int32_t n_kv, int32_t hd, int32_t
   return num_blocks >= 1 && num_blocks <= INT64_MAX / per_block;
 }
 
-// Default partition of the partition path: long enough to amortise a
-// workgroup (at most kDefaultPartition positions), short enough that the
-// grid of (partition, kv head, row) workgroups reaches kTargetWorkgroups
-// when rows are few.  From host shapes only.
+// Default partition length where the caller gives none and no other rule
+// applies (the stream path, which only keeps it for the record): long
+// enough to amortise a workgroup (at most kDefaultPartition positions),
+// short enough that the grid of (partition, kv head, row) workgroups reaches
+// kTargetWorkgroups when rows are few.  From host shapes only.
 int32_t default_partition(const pkv_attn_desc *d, int32_t cap) {
   const int64_t pairs = (int64_t)d->n_kv_heads * (d->rows > 0 ? d->rows : 1);
   const int64_t want_parts = (kTargetWorkgroups + pairs - 1) / pairs;
@@ -70,6 +71,21 @@ int32_t default_partition_mfma(const pkv_attn_desc *d, int32_t cap) {
   part = std::min<int64_t>(std::max<int64_t>(part, kMfmaMinPartition), kMfmaMaxPartition);
   part = (part + d->block_size - 1) / d->block_size * d->block_size;
   return (int32_t)part;
+}
+
+// Default partition of the VALU partition kernel (fp32, and bf16 head_dim
+// 16): about kValuPartitionBytes of K and V per partition, whatever the
+// batch.  Its workgroups are latency-bound, so they want many in flight;
+// the merge wants few partitions.  Measured (us, former default / this):
+// fp32 8 rows x 2 kv heads x hd 64 over 1024 positions 21.5 / 16.6 (128
+// positions), the same at 16 positions 10.3 / 6.5 (one partition), fp32 64
+// x 8 x hd 128 over 2048 276 / 253 (64), bf16 hd 16 32 x 8 over 4096 16.7 /
+// 15.5 (1024).
+constexpr int64_t kValuPartitionBytes = 64 << 10;
+int32_t default_partition_valu(const pkv_attn_desc *d, int32_t cap) {
+  int64_t part = kValuPartitionBytes / (2 * (int64_t)d->head_dim * elem_bytes(d->dtype));
+  part = std::max<int64_t>(part / d->block_size * d->block_size, d->block_size);
+  return (int32_t)std::min<int64_t>(part, cap);
 }
 
 constexpr int64_t kSmallBatchPairs = 256;   // (kv head, row) pairs
@@ -113,7 +129,8 @@ int plan_decode(const pkv_attn_desc *d, Plan *pl) {
   pl->stream = mfma && d->rows <= pkv::kPlanMaxRows && !small_batch &&
                cap_groups * d->n_kv_heads * d->rows < (int64_t)INT_MAX;
   int32_t part = d->partition_tokens;
-  if (part == 0) part = mfma && !pl->stream ? default_partition_mfma(d, cap) : default_partition(d, cap);
+  if (part == 0)
+    part = pl->stream ? default_partition(d, cap) : (mfma ? default_partition_mfma(d, cap) : default_partition_valu(d, cap));
   if (part < 0 || part % d->block_size != 0) return PKV_ERR_PARTITION;
   if (part > cap) part = cap;  // one partition covers every row: no split
   if (part / d->block_size > kMaxPartitionBlocks) return PKV_ERR_PARTITION;

@@ -65,20 +65,23 @@ def ws(lib, **kw):
 
 
 def test_workspace_size_partition_layout(lib):
-    # fp32 reads split rows into partitions: 64 rows x 32 heads x 8 partitions
-    # of 512 -> m and l (2 x 16384 floats), then 16384 rows of 128 partial sums
-    assert ws(lib, dtype=0, out_dtype=0) == (2 * 16384 + 16384 * 128) * 4
+    # fp32 reads split rows into partitions of about 64 KiB of K and V: at
+    # head_dim 128, 64 positions.  64 rows x 32 heads x 64 partitions -> m
+    # and l (2 x 131072 floats), then 131072 rows of 128 partial sums
+    assert ws(lib, dtype=0, out_dtype=0) == (2 * 131072 + 131072 * 128) * 4
+    # an explicit length: 8 partitions of 512
+    assert ws(lib, dtype=0, out_dtype=0, partition_tokens=512) == (2 * 16384 + 16384 * 128) * 4
     # one partition covers every row: no workspace
     assert ws(lib, dtype=0, partition_tokens=4096) == 0
-    assert ws(lib, dtype=0, max_blocks_per_row=32) == 0
+    assert ws(lib, dtype=0, max_blocks_per_row=4) == 0  # 64 positions
     # partitions of one block
     assert ws(lib, dtype=0, partition_tokens=16, max_blocks_per_row=4, rows=1, n_heads=2,
               n_kv_heads=1, head_dim=16) == (2 * 8 + 8 * 16) * 4
     # odd slot count: the partial sums start 16-byte aligned
     assert ws(lib, dtype=0, rows=1, n_heads=3, n_kv_heads=1, head_dim=16, partition_tokens=16,
               max_blocks_per_row=3) == (20 + 9 * 16) * 4
-    # bf16 with head_dim 16 takes the same layout
-    assert ws(lib, head_dim=16) == (2 * 16384 + 16384 * 16) * 4
+    # bf16 with head_dim 16 takes the same layout: 1024-position partitions
+    assert ws(lib, head_dim=16) == (2 * 8192 + 8192 * 16) * 4
     assert lib.pkv_paged_attention_workspace_size(None) == 0
     assert ws(lib, head_dim=96) == 0  # invalid descriptors need nothing
 

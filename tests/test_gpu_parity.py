@@ -230,9 +230,9 @@ def test_read_block_permutation_is_bitwise_invariant():
 def test_read_rows_are_independent(dtype, hd):
     # permuting and padding the batch leaves every row's result in place.  The
     # bf16 path balances work over the whole batch, so where a row is split --
-    # and hence its last bits -- may move; so does the default partition
-    # length of the fp32 path, which shrinks when rows are few.  With a fixed
-    # partition length the fp32 path splits every row the same way: bitwise.
+    # and hence its last bits -- may move.  The fp32 path's partition length
+    # depends on head_dim and dtype only, so it splits every row the same
+    # way whatever the batch: bitwise, with its default and a given length.
     cfg = small_cfg(dtype, rows=6, H=32, KV=8, hd=hd, bs=16, lo=1, hi=2000, seed=3)
     b = synth.make_batch(cfg, device=DEV)
     order = torch.tensor([5, 3, 1, 0, 2, 4, 0, 1], device=DEV)  # permuted and padded
@@ -245,6 +245,7 @@ def test_read_rows_are_independent(dtype, hd):
     got = gpu_read(b2, out_dtype=torch.float32)
     assert_close(got.cpu(), base[order].cpu(), what="rows", atol=2e-6, rtol=1e-5)
     if dtype == "f32":
+        assert torch.equal(base[order], got)
         base = gpu_read(b, out_dtype=torch.float32, partition=256)
         got = gpu_read(b2, out_dtype=torch.float32, partition=256)
         assert torch.equal(base[order], got)
