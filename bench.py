@@ -33,7 +33,7 @@ HBM_PEAK_GBS = 8000.0
 # a plain copy of known size (profiles/decode_stream_<workload>_hbm_counters.md),
 # valid only for the kernel sources they were taken on.
 PROFILED_TRAFFIC = {
-    "llama3_8b_layer": {"src": "b4994ceff29d725a", "read_bytes": 577504791},
+    "llama3_8b_layer": {"src": "1d31811046ac3ddf", "read_bytes": 577518977},
 }
 KERNEL_SOURCES = ("decode.hip", "pkv_internal.h", "abi.hip")
 
