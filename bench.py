@@ -66,6 +66,8 @@ def parse():
                     help="target CPU time of the oracle baseline (0 disables it)")
     ap.add_argument("--headline-only", action="store_true",
                     help="skip the other workloads (small fp32 reads, skewed batch, decode runs)")
+    ap.add_argument("--prompt-scatter-only", action="store_true",
+                    help="time only the 65536-token prompt scatter (for profiling)")
     ap.add_argument("--prefill-chunk-only", action="store_true",
                     help="only time the multi-query read of a 64-query chunk over 16 rows of the 8B "
                          "layer (the prefill_chunk entry of other_workloads) and print it")
@@ -201,8 +203,33 @@ def other_workloads(dev, stream):
             del run, out, steps
     res["decode_run"] = runs
     res["decode_step_graph"] = graph_step(dev, stream)
+    res["prompt_scatter"] = prompt_scatter(dev, stream)
     res["prefill_chunk"] = prefill_chunk(dev, stream)
     return res
+
+
+def prompt_scatter(dev, stream, rows=128, prompt=512, calls=20):
+    """The slot-mapping scatter of a whole prompt batch (rows x prompt tokens,
+    each row's prompt in consecutive slots of its blocks, 8 kv heads, head_dim
+    128, bf16, blocks of 16): µs per call and the HBM rate of the bytes it
+    must move (K and V read once and written once, plus the slots)."""
+    import torch
+
+    import paged_kv_cache_13_amd as pkv
+    from paged_kv_cache_13_amd import harness, synth
+
+    run = synth.DecodeRun(rows=rows, block_size=16, prompt=prompt, steps=0, device=dev, seed=11)
+    k, v, slots = run.prefill()
+
+    def call():
+        pkv.reshape_and_cache(k, v, slots, run.k_pool, run.v_pool)
+
+    for _ in range(3):
+        call()
+    mean, med = _timed(call, stream, calls, lead_cycles=1000000)
+    nb = harness.scatter_bytes(k.shape[0], k.shape[1], k.shape[2], 2)
+    return {"tokens": int(k.shape[0]), "bytes": nb, "us": round(mean, 2), "us_median": round(med, 2),
+            "GB/s": round(nb / (mean * 1e-6) / 1e9, 1)}
 
 
 def prefill_chunk(dev, stream, rows=16, qlen=64):
@@ -323,6 +350,10 @@ def main():
                           "copy_calibration_bytes_written": dst.numel() * 4, "calls": 5}))
         return
     pkv.load_library()
+    if args.prompt_scatter_only:
+        stream = torch.cuda.current_stream()
+        print(json.dumps({"prompt_scatter": prompt_scatter(dev, stream)}), flush=True)
+        return
     if args.prefill_chunk_only:
         stream = torch.cuda.current_stream()
         print(json.dumps({"prefill_chunk": prefill_chunk(dev, stream)}), flush=True)
