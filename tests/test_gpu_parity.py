@@ -487,6 +487,26 @@ def test_read_many_rows(rows, width):
     assert (b.ctx_host == 0).any()
 
 
+@pytest.mark.parametrize("hd,KV", [(128, 2), (64, 1)])
+def test_read_more_rows_than_the_plan_holds(hd, KV):
+    # 8200 rows (over the 8192 a plan kernel holds) over a 2048-position
+    # table: the MFMA partition kernel at a large grid.  Lengths are short,
+    # so the pool stays small; the table's unused entries point at NaN.
+    rows = 8200
+    lens = np.random.default_rng(hd).integers(0, 120, size=rows)
+    lens[[0, 17, rows - 1]] = [0, 1, 119]
+    cfg = synth.DecodeConfig("rows8k", "bf16", rows=rows, n_heads=8, n_kv_heads=KV, head_dim=hd,
+                             block_size=16, ctx=("fixed", tuple(int(x) for x in lens)),
+                             pool=("factor", 1.5), max_ctx=2048, seed=hd)
+    b = synth.make_batch(cfg, device=DEV)
+    sample = np.unique(np.concatenate([[0, 1, 17, 4095, 4096, 8191, 8192, rows - 1],
+                                       np.random.default_rng(2).choice(rows, 16, replace=False)]))
+    ref = oracle_read(b, sample)
+    got = gpu_read(b, out_dtype=torch.float32)[torch.as_tensor(sample, device=DEV)].cpu().numpy()
+    assert_close(got, ref, what="rows=%d hd=%d" % (rows, hd), **TOL[torch.float32])
+    assert np.array_equal(got[0], np.zeros_like(got[0]))  # the empty row
+
+
 # ---------------------------------------------------------------------------
 # multi-query read (a chunk of queries per row, causal inside the chunk)
 # ---------------------------------------------------------------------------
