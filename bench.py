@@ -29,11 +29,12 @@ sys.path.insert(0, ROOT)
 METRIC = "paged decode read µs/call + achieved HBM GB/s (% peak), 8B-shaped layer"
 HBM_PEAK_GBS = 8000.0
 
-# HBM bytes per read measured with rocprofv3 FETCH_SIZE + WRITE_SIZE, scaled by
-# a plain copy of known size (profiles/decode_stream_<workload>_hbm_counters.md),
-# valid only for the kernel sources they were taken on.
+# HBM bytes per one-call decode step and per plain read, measured with
+# rocprofv3 FETCH_SIZE + WRITE_SIZE and scaled by a plain copy of known size
+# (profiles/decode_stream_<workload>_hbm_counters.md), valid only for the
+# kernel sources they were taken on.
 PROFILED_TRAFFIC = {
-    "llama3_8b_layer": {"src": "1d31811046ac3ddf", "read_bytes": 577518977},
+    "llama3_8b_layer": {"src": "1d31811046ac3ddf", "step_bytes": 580473763, "read_bytes": 577518977},
 }
 KERNEL_SOURCES = ("decode.hip", "pkv_internal.h", "abi.hip")
 
@@ -50,7 +51,7 @@ def profiled_traffic(workload):
     rec = PROFILED_TRAFFIC.get(workload)
     if rec is None or rec["src"] != kernel_source_hash():
         return None
-    return rec["read_bytes"]
+    return rec["step_bytes"]
 
 
 def parse():
@@ -393,22 +394,32 @@ def main():
 
     # the timed steps: wall clock over K back-to-back steps
     K = args.steps
-    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(K)]
+    mk_events = lambda: [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                         for _ in range(K)]
+    region = (torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    for i in range(K):
+    region[0].record(stream)
+    for i in range(K):  # the timed steps, back to back
         step()
+    region[1].record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
-    # the read alone, K calls, each bracketed by HIP events on its stream
+    region_ms = region[0].elapsed_time(region[1])
+
+    def per_call(fn):  # K more calls, each bracketed by HIP events on its stream
+        ev = mk_events()
+        for i in range(K):
+            ev[i][0].record(stream)
+            fn()
+            ev[i][1].record(stream)
+        torch.cuda.synchronize()
+        return np.array([a.elapsed_time(b) for a, b in ev])
+
+    step_ms = per_call(step)  # the step's kernels, launch by launch
     for _ in range(args.warmup):
         read()
-    for i in range(K):
-        ev[i][0].record(stream)
-        read()
-        ev[i][1].record(stream)
-    torch.cuda.synchronize()
-    read_ms = np.array([a.elapsed_time(b) for a, b in ev])
+    read_ms = per_call(read)  # the read alone
 
     # reads with the Infinity Cache flushed (a 512 MiB write) before each
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
@@ -427,7 +438,8 @@ def main():
     sb = harness.scatter_bytes(cfg.rows, cfg.n_kv_heads, cfg.head_dim, elem)
     ms_step = wall * 1e3 / K
     read_us = float(read_ms.mean() * 1e3)
-    achieved = rb / (read_us * 1e-6) / 1e9
+    step_us = float(step_ms.mean() * 1e3)
+    achieved = (rb + sb) / (step_us * 1e-6) / 1e9
     stats = pkv.ReadCounters("streamed", block=bs)
     stats.record(cfg.rows, cfg.n_heads, 1, int(batch.ctx_host.max()))
     print("readstats: mode=%s block=%d calls=%d rows=%d score_cells=%d held_cells=%d saving=%.1fx"
@@ -457,14 +469,18 @@ def main():
         "read_us_p10": round(float(np.percentile(read_ms, 10)) * 1e3, 2),
         "read_us_p90": round(float(np.percentile(read_ms, 90)) * 1e3, 2),
         "read_us_flushed": round(float(np.median(fl_ms)) * 1e3, 2) if fl_ms else None,
-        "read_pct_peak": round(100 * achieved / HBM_PEAK_GBS, 2),
+        "read_pct_peak": round(100 * rb / (read_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 2),
         "read_bytes": rb,
         "scatter_bytes": sb,
+        "step_us": round(step_us, 2),
+        "step_us_median": round(float(np.median(step_ms)) * 1e3, 2),
+        "step_us_timed_region": round(region_ms * 1e3 / K, 2),
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
                      "traffic": profiled_traffic(cfg.name),
-                     "kernel": "paged decode read call (decode_stream + decode_stream_merge)",
-                     "bytes_per_launch": rb, "us_per_launch": round(read_us, 2)},
+                     "kernel": "one-call decode step: decode_stream (appending the step's tokens) + "
+                               "decode_stream_merge",
+                     "bytes_per_launch": rb + sb, "us_per_launch": round(step_us, 2)},
     }
     if args.cpu_seconds > 0:
         res["cpu_baseline"] = cpu_baseline(batch, new_k, new_v, slots_h, args.cpu_seconds)
