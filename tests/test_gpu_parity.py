@@ -487,6 +487,56 @@ def test_read_many_rows(rows, width):
     assert (b.ctx_host == 0).any()
 
 
+@pytest.mark.parametrize("name", ["llama3_8b_layer", "skewed_long"])
+def test_stream_read_ignores_stale_workspace(name):
+    # a row cut into several slices is merged by the slice that arrives last
+    # on the row's arrival word, which carries the dispatch's tag: whatever
+    # the workspace holds beforehand (zeros, all ones, random bytes, the words
+    # of a read of other lengths, on this stream or another), the bits agree
+    b = synth.make_batch(synth.CONFIGS[name], device=DEV)
+    other = synth.make_batch(synth.CONFIGS[name], device=DEV, seed=synth.CONFIGS[name].seed + 11)
+    n = max(pkv.workspace_size(b.q, b.k_pool, b.block_table), pkv.workspace_size(other.q, other.k_pool,
+                                                                                  other.block_table), 1)
+    ref = gpu_read(b, out_dtype=torch.float32)
+    g = torch.Generator().manual_seed(7)
+    fills = {"zeros": torch.zeros(n, dtype=torch.uint8), "ones": torch.full((n,), 255, dtype=torch.uint8),
+             "random": torch.randint(0, 256, (n,), dtype=torch.uint8, generator=g)}
+    side = torch.cuda.Stream()
+    for what, fill in fills.items():
+        ws = fill.to(DEV)
+        for i in range(3):
+            out = torch.full(b.q.shape, float("nan"), dtype=torch.float32, device=DEV)
+            if i == 1:  # the words of a read of other lengths, then this read on another stream
+                scratch = torch.empty(other.q.shape, dtype=torch.float32, device=DEV)
+                pkv.paged_attention_into(other.q, other.k_pool, other.v_pool, other.block_table,
+                                         other.context_lens, other.scale, scratch, workspace=ws)
+                side.wait_stream(torch.cuda.current_stream())
+                with torch.cuda.stream(side):
+                    pkv.paged_attention_into(b.q, b.k_pool, b.v_pool, b.block_table, b.context_lens, b.scale,
+                                             out, workspace=ws)
+                torch.cuda.current_stream().wait_stream(side)
+            else:
+                pkv.paged_attention_into(b.q, b.k_pool, b.v_pool, b.block_table, b.context_lens, b.scale, out,
+                                         workspace=ws)
+            torch.cuda.synchronize()
+            assert torch.equal(out, ref), "%s %s call %d" % (name, what, i)
+
+
+@pytest.mark.parametrize("rows,KV,ctx", [(1, 1, 32768), (2, 2, 20000), (3, 8, 4097)])
+def test_read_row_cut_into_many_slices(rows, KV, ctx):
+    # few (kv head, row) pairs over long tables: each pair is cut into up to
+    # hundreds of slices, all counting on one arrival word, and merged in
+    # batches of slices
+    cfg = synth.DecodeConfig("many_slices", "bf16", rows=rows, n_heads=4 * KV, n_kv_heads=KV, head_dim=128,
+                             block_size=16, ctx=("fixed", tuple([ctx] * rows)), pool=("factor", 1.0),
+                             max_ctx=ctx, value_scale=0.5, seed=rows * 7 + KV)
+    b = synth.make_batch(cfg, device=DEV)
+    ref = oracle_read(b, np.arange(rows))
+    got = gpu_read(b, out_dtype=torch.float32).cpu().numpy()
+    assert_close(got, ref, what="rows=%d KV=%d ctx=%d" % (rows, KV, ctx), **TOL[torch.float32])
+    assert torch.equal(torch.from_numpy(got), gpu_read(b, out_dtype=torch.float32).cpu())
+
+
 @pytest.mark.parametrize("hd,KV", [(128, 2), (64, 1)])
 def test_read_more_rows_than_the_plan_holds(hd, KV):
     # 8200 rows (over the 8192 a plan kernel holds) over a 2048-position
