@@ -254,7 +254,7 @@ def prefill_chunk(dev, stream, rows=16, qlen=64):
         pkv.paged_attention_multi(q, b.k_pool, b.v_pool, b.block_table, b.context_lens, b.scale, out=out,
                                   workspace=ws)
 
-    for _ in range(3):
+    for _ in range(10):  # the first calls on fresh pools run 5-12 % slow
         call()
     mean, med = _timed(call, stream, 20)
     kv = harness.read_bytes(b.ctx_host, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim, cfg.block_size, 2, 2)

@@ -164,9 +164,17 @@ int plan_decode(const pkv_attn_desc *d, Plan *pl) {
 // rounded up to a group (and capped), else the power of two (256 .. 2048)
 // nearest below the one that makes the largest possible grid about one
 // workgroup per slot of the GPU (kComputeUnits compute units times the
-// workgroups of this shape one unit holds).  Larger partitions mean fewer
-// start-ups and partial results; measured on the 8B shape, one slot per
-// workgroup beat both finer and coarser cuts.
+// workgroups of this shape one unit holds), and 1024 at most for two-wave
+// workgroups.  Larger partitions mean fewer start-ups and partial results.
+// Measured on the 8B shape (lengths uniform in [512, 4096]), us per call
+// for partitions of 256 / 512 / 1024 / 2048 positions (* = this rule):
+//   16 rows x 64 queries  207.5 / 142.3 / 120.4 / 105.8*
+//   64 rows x 64 queries  736.9 / 517.0 / 391.3 / 355.6*
+//    4 rows x 64 queries   60.5 /  43.6* /  57.3 /  90.2
+//   64 rows x 32 queries  442.0 / 321.4 / 271.2 / 253.9*
+//   16 rows x 16 queries   73.8 /  58.6 /  52.1* /  81.4
+//   64 rows x 16 queries  244.0 / 199.6 / 171.6* / 180.3
+//   64 rows x  8 queries  205.2 / 176.2 / 158.9* / 171.1
 constexpr int64_t kComputeUnits = 256;
 constexpr int64_t kStreamMultiGroups = 32;
 struct MultiPlan {
@@ -209,8 +217,10 @@ int plan_multi(const pkv_attn_desc *d, int32_t query_len, Plan *pl, MultiPlan *m
     const int64_t blocks = (int64_t)mp->q_blocks * d->n_kv_heads * (d->rows > 0 ? d->rows : 1);
     const int64_t per_cu = std::max<int64_t>(1, (d->head_dim == 128 ? 4 : 8) / waves);  // registers, LDS
     const int64_t want = (int64_t)cap * blocks / (kComputeUnits * per_cu);
+    // two-wave workgroups (at most two tiles) stop at 1024 positions
+    const int64_t top = waves <= 2 ? 1024 : 2048;
     part = 256;
-    while (part < 2048 && part * 2 <= want) part *= 2;
+    while (part < top && part * 2 <= want) part *= 2;
   }
   if (part > pkv::kMultiMaxPartition) part = pkv::kMultiMaxPartition;
   if (part < g32) part = g32;

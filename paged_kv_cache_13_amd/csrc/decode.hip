@@ -1845,7 +1845,10 @@ __device__ __forceinline__ void multi_pair(MultiState<HD> &S, const uint4 *c0, c
   }
   // Weights (below 2^kLazyRescale), this lane's part of the row sum, hi/lo
   // split, then the P.V products.  A -inf score gives weight 0; a column that
-  // has seen nothing yet takes 0 as its reference.
+  // has seen nothing yet takes 0 as its reference.  For a bf16 output the lo
+  // half is skipped: P rounded to bf16 moves the result by at most 2^-9
+  // max|V|, below the output's own rounding for |V| ~ |out|, and saves a
+  // third of the matrix-core work.  An fp32 output keeps both halves.
   const float mref = S.m == -INFINITY ? 0.f : S.m;
   float p0[16], p1[16];
 #pragma unroll
@@ -1869,11 +1872,14 @@ __device__ __forceinline__ void multi_pair(MultiState<HD> &S, const uint4 *c0, c
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt)
       S.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc[dt][kk], phi0[kk], S.acc[dt], 0, 0, 0);
+  const bool exact = a.out_dtype == kF32;
+  if (exact) {
 #pragma unroll
-  for (int kk = 0; kk < 2; ++kk)
+    for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-      S.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc[dt][kk], plo0[kk], S.acc[dt], 0, 0, 0);
+      for (int dt = 0; dt < DT; ++dt)
+        S.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc[dt][kk], plo0[kk], S.acc[dt], 0, 0, 0);
+  }
   if (two) {
     multi_v<HD>(vc, c1, gb1, n, lane);
 #pragma unroll
@@ -1881,11 +1887,13 @@ __device__ __forceinline__ void multi_pair(MultiState<HD> &S, const uint4 *c0, c
 #pragma unroll
       for (int dt = 0; dt < DT; ++dt)
         S.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc[dt][kk], phi1[kk], S.acc[dt], 0, 0, 0);
+    if (exact) {
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk)
+      for (int kk = 0; kk < 2; ++kk)
 #pragma unroll
-      for (int dt = 0; dt < DT; ++dt)
-        S.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc[dt][kk], plo1[kk], S.acc[dt], 0, 0, 0);
+        for (int dt = 0; dt < DT; ++dt)
+          S.acc[dt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(vc[dt][kk], plo1[kk], S.acc[dt], 0, 0, 0);
+    }
   }
 }
 

@@ -285,9 +285,9 @@ def test_multi_query_workspace(lib):
     # 8 queries (32 columns): the workgroup path.  64 rows x 8 kv heads x one
     # query block (a two-wave workgroup, two per compute unit) = 512 blocks
     # on 512 slots: a 4096-position table wants 4096-position partitions,
-    # capped at 2048, so it splits in 2: m, l and a 128-float acc per (row,
-    # query, head, partition)
-    slots = 64 * 8 * 32 * 2
+    # capped at 1024 for two-wave workgroups, so it splits in 4: m, l and a
+    # 128-float acc per (row, query, head, partition)
+    slots = 64 * 8 * 32 * 4
     assert ws(d, 8) == (((2 * slots + 3) & ~3) + slots * 128) * 4
     # 16 rows: 128 blocks want 1024-position partitions (4 of them)
     slots16 = 16 * 8 * 32 * 4
