@@ -1224,10 +1224,12 @@ __global__ __launch_bounds__(256) void decode_stream_merge(DecodeArgs a) {
     // groups per kv head and before row r, by a block reduction over the
     // (at most 256) clamped lengths
     __shared__ int s_red[2][256 / kWave];
+    __shared__ int s_len;
     const int cap = a.max_blocks_per_row * a.block_size;
     const int t = threadIdx.x;
     int x = t < a.rows ? a.context_lens[t] : 0;
     x = x < 0 ? 0 : (x > cap ? cap : x);
+    if (t == r) s_len = x;  // row r's length, across the barrier below (no second load)
     const int gx = (x + kGroupPositions - 1) / kGroupPositions;
     int tot = gx, pre = t < r ? gx : 0;
 #pragma unroll
@@ -1242,9 +1244,7 @@ __global__ __launch_bounds__(256) void decode_stream_merge(DecodeArgs a) {
     __syncthreads();
     ngk = s_red[0][0] + s_red[0][1] + s_red[0][2] + s_red[0][3];
     g0 = s_red[1][0] + s_red[1][1] + s_red[1][2] + s_red[1][3];
-    int xr = a.context_lens[r];
-    xr = xr < 0 ? 0 : (xr > cap ? cap : xr);
-    ng = (xr + kGroupPositions - 1) / kGroupPositions;
+    ng = (s_len + kGroupPositions - 1) / kGroupPositions;
     const long long all = (long long)a.n_kv_heads * ngk;
     waves = all / max(a.cg_min, 1);
     waves = waves < 1 ? 1 : (waves > kStreamWaves ? kStreamWaves : waves);
@@ -2059,15 +2059,40 @@ __global__ __launch_bounds__(256) void decode_multi_merge(DecodeArgs a) {
   if (nparts <= 1) return;  // written directly by decode_multi
   const WsLayout W = ws_layout(a.rows * Q, a.n_heads, a.max_parts, HD);
   const size_t s0 = vh * a.max_parts;
-  float M = -INFINITY;
-  for (int j0 = 0; j0 < nparts; j0 += 32)
+  float M = -INFINITY;  // the general path's maximum (more than four partitions)
+  for (int j0 = 0; j0 < nparts && nparts > 4; j0 += 32)
     if (j0 + sub < nparts) M = fmaxf(M, a.ws[W.m_off + s0 + j0 + sub]);
 #pragma unroll
   for (int x = 16; x >= 1; x >>= 1) M = fmaxf(M, __shfl_xor(M, x, 32));
   const int d = 4 * sub;  // this lane's hd values d .. d + 3
   float L = 0.f;
   f32x4_t O = {0.f, 0.f, 0.f, 0.f};
-  for (int j0 = 0; j0 < nparts; j0 += 32) {
+  if (nparts <= 4) {
+    // every load in one round trip: m and l of partition `sub`, and this
+    // lane's acc values of all partitions (none depends on the maximum);
+    // then the same arithmetic, in the same order, as the general loop
+    const bool own = sub < nparts;
+    const float mj = own ? a.ws[W.m_off + s0 + sub] : -INFINITY;
+    const float lj = own ? a.ws[W.l_off + s0 + sub] : 0.f;
+    const float *acc = a.ws + W.acc_off + s0 * HD + d;
+    f32x4_t x[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      x[u] = u < nparts && d < HD ? *reinterpret_cast<const f32x4_t *>(acc + (size_t)u * HD)
+                                  : f32x4_t{0.f, 0.f, 0.f, 0.f};
+    float M = mj;
+#pragma unroll
+    for (int x2 = 16; x2 >= 1; x2 >>= 1) M = fmaxf(M, __shfl_xor(M, x2, 32));
+    float w = 0.f;
+    if (own && M != -INFINITY) {
+      w = mj == -INFINITY ? 0.f : exp2_fast(mj - M);
+      L = fmaf(lj, w, L);
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (u < nparts) O += __shfl(w, u, 32) * x[u];
+  }
+  for (int j0 = 0; j0 < nparts && nparts > 4; j0 += 32) {
     float w = 0.f;
     if (j0 + sub < nparts && M != -INFINITY) {
       const float mj = a.ws[W.m_off + s0 + j0 + sub];
