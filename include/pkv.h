@@ -172,6 +172,11 @@ size_t pkv_paged_attention_workspace_size(const pkv_attn_desc *d);
  * A query with p < 0 (a row shorter than the chunk) reads zeros.  With
  * query_len = 1 this is pkv_paged_attention.
  *
+ * Precision: scores, softmax and sums in fp32.  For a bf16 out the weights
+ * enter the P.V product rounded to bf16 (a change of at most 2^-9 max|V|,
+ * the size of the output's own rounding); for an fp32 out they keep 16
+ * significant bits (a bf16 hi + lo pair).
+ *
  *   d             as for pkv_paged_attention; dtype must be PKV_BF16 and
  *                 head_dim 64 or 128 (else PKV_ERR_DTYPE / PKV_ERR_HEAD_DIM);
  *                 partition_tokens is rounded up to a multiple of 32 and
