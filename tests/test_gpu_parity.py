@@ -329,6 +329,8 @@ def equal_nan(a, b):
     (300, 16, 1040, 128, "bf16"),  # more rows than a wave plans for: the plan kernel runs first
     (16, 16, 70, 16, "bf16"),    # head_dim 16: the VALU partition kernel appends
     (16, 16, 70, 64, "f32"),     # fp32: the VALU partition kernel appends
+    (128, 16, 200, 128, "bf16"),  # 1024 partition workgroups: more than one round on the GPU
+    (96, 8, 150, 64, "f32"),     # fp32, 1536 VALU partition workgroups
 ])
 def test_decode_step_equals_scatter_then_read(rows, bs, prompt, hd, dtype):
     # bitwise: the one-call step, whose read appends the tokens itself,
