@@ -72,41 +72,85 @@ def parse():
     ap.add_argument("--prefill-chunk-only", action="store_true",
                     help="only time the multi-query read of a 64-query chunk over 16 rows of the 8B "
                          "layer (the prefill_chunk entry of other_workloads) and print it")
+    ap.add_argument("--graph-step-only", action="store_true",
+                    help="only time the 8B layer's one-call decode step eager and replayed from a "
+                         "captured HIP graph (the decode_step_graph entry of other_workloads) and print it")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a plain 256 MiB device-to-device copy 5 times (a kernel of "
                          "known traffic, to scale HBM counters by) and exit")
     return ap.parse_args()
 
 
+def cpu_threads():
+    """Host threads for the parallel oracle leg: the cores this process may
+    run on, at most 16 (one GPU's share of its host)."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
 def cpu_baseline(batch, new_k, new_v, slots_h, budget_s):
-    """The CPU oracle (plain C, one thread) on the same inputs, copied to host
+    """The CPU oracle (plain C, fp64) on the same inputs, copied to host
     memory outside the timing: scatter of the step's new tokens, then the read
-    of every row.  Repeated until about `budget_s` seconds of CPU work."""
+    of every row.  Two legs: one thread, repeated until about `budget_s` / 2
+    seconds of CPU work; then every host core this process may use, each
+    thread calling the unchanged oracle on its share of the rows (rows
+    i, i + T, ...; ctypes releases the GIL during the call), for about as
+    long.  The parallel leg is the reported value."""
+    import concurrent.futures
+
+    import numpy as np
+    import torch
+
     import oracle
     from paged_kv_cache_13_amd import harness
 
     oracle.build()
+    oracle._load()
     q = batch.q.cpu()
     kp = batch.k_pool.cpu()
     vp = batch.v_pool.cpu()
     kn, vn = new_k.cpu(), new_v.cpu()
     cfg = batch.cfg
-    reps, spent = 0, 0.0
-    while spent < budget_s and (reps == 0 or spent / reps * (reps + 1) <= 2 * budget_s):
-        t0 = time.perf_counter()
-        oracle.reshape_and_cache(kn, vn, slots_h, kp, vp)
-        oracle.paged_attention(q, kp, vp, batch.table_host, batch.ctx_host, batch.scale)
-        spent += time.perf_counter() - t0
-        reps += 1
     nbytes = harness.read_bytes(batch.ctx_host, cfg.n_heads, cfg.n_kv_heads, cfg.head_dim,
                                 cfg.block_size, 2, 2)
     nbytes += harness.scatter_bytes(cfg.rows, cfg.n_kv_heads, cfg.head_dim, 2)
-    per = spent / reps
-    return {"value": round(nbytes / per / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "ms_per_step": round(per * 1e3, 2),
-            "sample": "the full workload (%d rows, sum ctx %d), %d step(s): scatter + read, "
-                      "single-threaded C in fp64" % (cfg.rows, int(batch.ctx_host.sum()), reps),
-            "cpu": cpu_model()}
+
+    def repeat(step, budget):
+        reps, spent = 0, 0.0
+        while spent < budget and (reps == 0 or spent / reps * (reps + 1) <= 2 * budget):
+            t0 = time.perf_counter()
+            step()
+            spent += time.perf_counter() - t0
+            reps += 1
+        return spent / reps, reps
+
+    def serial_step():
+        oracle.reshape_and_cache(kn, vn, slots_h, kp, vp)
+        oracle.paged_attention(q, kp, vp, batch.table_host, batch.ctx_host, batch.scale)
+
+    threads = cpu_threads()
+    shares = [np.arange(i, cfg.rows, threads) for i in range(threads)]
+    shares = [(q[torch.from_numpy(ix)], batch.table_host[ix], batch.ctx_host[ix]) for ix in shares if ix.size]
+    pool = concurrent.futures.ThreadPoolExecutor(len(shares))
+
+    def parallel_step():
+        oracle.reshape_and_cache(kn, vn, slots_h, kp, vp)
+        list(pool.map(lambda s: oracle.paged_attention(s[0], kp, vp, s[1], s[2], batch.scale), shares))
+
+    one_s, one_reps = repeat(serial_step, budget_s / 2)
+    par_s, par_reps = repeat(parallel_step, budget_s / 2)
+    pool.shutdown()
+    return {"value": round(nbytes / par_s / 1e9, 4), "unit": "GB/s", "cores": len(shares), "kind": "oracle",
+            "ms_per_step": round(par_s * 1e3, 2),
+            "sample": "the full workload (%d rows, sum ctx %d): scatter + read per step, plain C in fp64; "
+                      "%d step(s) on %d threads (rows split round-robin), %d step(s) on one thread"
+                      % (cfg.rows, int(batch.ctx_host.sum()), par_reps, len(shares), one_reps),
+            "single_thread": {"value": round(nbytes / one_s / 1e9, 4), "unit": "GB/s", "cores": 1,
+                              "ms_per_step": round(one_s * 1e3, 2)},
+            "nproc": os.cpu_count(), "cpu": cpu_model()}
 
 
 def _timed(fn, stream, calls, lead_cycles=200000):
@@ -172,8 +216,8 @@ def other_workloads(dev, stream):
                 bt, cl = run.block_table(), run.context_lens()
                 ws = torch.zeros(max(pkv.workspace_size(q, run.k_pool, bt), 1), dtype=torch.uint8, device=dev)
                 steps.append((q, kn, vn, sl, bt, cl, ws, run.ctx_host.copy()))
-            stats = pkv.ReadCounters("streamed", block=bs)
             out = torch.empty(rows, run.n_heads, run.head_dim, dtype=torch.bfloat16, device=dev)
+            stats = pkv.ReadCounters("streamed", block=pkv.read_tile(out, run.k_pool, steps[0][4]))
             t_sc, t_rd, t_step, t_rect, rbytes = [], [], [], [], 0
             for q, kn, vn, sl, bt, cl, ws, ctx in steps:
                 # the step as one call first, then again as a scatter and a read
@@ -266,10 +310,14 @@ def prefill_chunk(dev, stream, rows=16, qlen=64):
             "TFLOP/s": round(flops / (mean * 1e-6) / 1e12, 2)}
 
 
-def graph_step(dev, stream, reps=100):
+def graph_step(dev, stream, reps=100, per_graph=8):
     """The 8B-shaped layer's whole decode step (scatter + read) as one library
-    call, eager and replayed from a captured HIP graph: GPU µs per step (events,
-    host ahead) and wall-clock µs per step for back-to-back steps."""
+    call, eager and replayed from captured HIP graphs: GPU µs per step (events,
+    host ahead) and wall-clock µs per step for back-to-back steps.  Each graph
+    launch costs a fixed gap before its first kernel (about 8 us in a kernel
+    trace on this runtime), so a graph of one step pays it every step; a graph
+    of `per_graph` steps (as a serving loop would capture many layers) pays it
+    once for all of them."""
     import torch
 
     import paged_kv_cache_13_amd as pkv
@@ -301,19 +349,27 @@ def graph_step(dev, stream, reps=100):
     graph = torch.cuda.CUDAGraph()
     with torch.cuda.graph(graph):
         step()
+    graph_n = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph_n):
+        for _ in range(per_graph):
+            step()
     for _ in range(10):
         graph.replay()
+        graph_n.replay()
     graph_us, _ = _timed(graph.replay, stream, 50)
+    graph_n_us, _ = _timed(graph_n.replay, stream, 20)
     walls = {}
-    for name, fn in (("eager", step), ("graph", graph.replay)):
+    for name, fn, n in (("eager", step, 1), ("graph", graph.replay, 1), ("graph_n", graph_n.replay, per_graph)):
         torch.cuda.synchronize()
         t0 = time.perf_counter()
-        for _ in range(reps):
+        for _ in range(reps // n):
             fn()
         torch.cuda.synchronize()
-        walls[name] = (time.perf_counter() - t0) / reps * 1e6
+        walls[name] = (time.perf_counter() - t0) / (reps // n * n) * 1e6
     return {"workload": cfg.name, "eager_step_us": round(eager_us, 2), "graph_step_us": round(graph_us, 2),
-            "eager_wall_us_per_step": round(walls["eager"], 2), "graph_wall_us_per_step": round(walls["graph"], 2)}
+            "graph_%d_steps_us_per_step" % per_graph: round(graph_n_us / per_graph, 2),
+            "eager_wall_us_per_step": round(walls["eager"], 2), "graph_wall_us_per_step": round(walls["graph"], 2),
+            "graph_%d_steps_wall_us_per_step" % per_graph: round(walls["graph_n"], 2)}
 
 
 def cpu_model():
@@ -358,6 +414,10 @@ def main():
     if args.prefill_chunk_only:
         stream = torch.cuda.current_stream()
         print(json.dumps({"prefill_chunk": prefill_chunk(dev, stream)}), flush=True)
+        return
+    if args.graph_step_only:
+        stream = torch.cuda.current_stream()
+        print(json.dumps({"decode_step_graph": graph_step(dev, stream)}), flush=True)
         return
     cfg = synth.CONFIGS[args.workload]
     batch = synth.make_batch(cfg, device=dev)
@@ -440,7 +500,7 @@ def main():
     read_us = float(read_ms.mean() * 1e3)
     step_us = float(step_ms.mean() * 1e3)
     achieved = (rb + sb) / (step_us * 1e-6) / 1e9
-    stats = pkv.ReadCounters("streamed", block=bs)
+    stats = pkv.ReadCounters("streamed", block=pkv.read_tile(batch.q, batch.k_pool, batch.block_table))
     stats.record(cfg.rows, cfg.n_heads, 1, int(batch.ctx_host.max()))
     print("readstats: mode=%s block=%d calls=%d rows=%d score_cells=%d held_cells=%d saving=%.1fx"
           % (stats.mode, stats.block, stats.calls, stats.rows, stats.score_cells, stats.held_cells,

@@ -14,9 +14,10 @@
  *     softmax instead of materialising the history; section "Diagram": the
  *     result goes back to grouped-query attention;
  *   - "Day 60: the read becomes a choice, and a counter is what can see it",
- *     section "What I added today": the streamed read never builds the
- *     [rows, heads, 1, ctx] score rectangle; section "Why it matters": the
- *     read must not read device values back on the host (no sync).
+ *     section "What I added today": where the gathered read scores a whole
+ *     rows x heads x 1 x ctx rectangle at once, the streamed read keeps one
+ *     tile of scores per row and head; section "Why it matters": the read
+ *     must not read device values back on the host (no sync).
  *
  * Layout (all buffers device memory, row-major, contiguous, 16-byte aligned):
  *   k_pool         : [num_blocks, n_kv_heads, block_size, head_dim]
@@ -25,6 +26,15 @@
  *                    it K is position-major and V dimension-major, so both
  *                    contractions of the read find their reduction index
  *                    contiguous: head_dim for q.K, positions for p.V)
+ *   The V pool departs from the position-major [num_blocks, n_kv_heads,
+ *   block_size, head_dim] pool of the nanoserve-style interface (the pages
+ *   name no layout; slot semantics are the same).  The trade, measured on an
+ *   8B-shaped layer (64 rows, 8 kv heads, head_dim 128, bf16): the read's
+ *   P.V fragments load as contiguous 16-byte runs, while appending a token
+ *   writes its V row as head_dim 2-byte stores block_size elements apart --
+ *   a decode step's 64 tokens (0.26 MB of K + V) cost about 2.2 MB of HBM
+ *   writes and 2.9 us of a 100 us step.  A caller holding position-major V
+ *   pools must transpose them once; the scatter below writes this layout.
  *   q, out         : [rows, n_heads, head_dim]
  *   k, v (scatter) : [num_tokens, n_kv_heads, head_dim]
  *   slot_mapping   : [num_tokens] int64; slot s = block * block_size + offset
@@ -90,11 +100,29 @@ typedef struct pkv_attn_desc {
   int32_t out_dtype;          /* pkv_dtype of out (normally == dtype) */
   int32_t partition_tokens;   /* split-context partition length in positions,
                                  a positive multiple of block_size, or 0 for the
-                                 library default: bf16 head_dim 64/128 reads cut
-                                 rows into slices of at least 128 positions;
-                                 other reads use partitions of at most 512
-                                 positions, shorter when rows x kv heads are
-                                 too few to fill the GPU */
+                                 library default, which depends on the path the
+                                 read takes (host shapes only; "table" below is
+                                 max_blocks_per_row * block_size positions):
+                                 - bf16, head_dim 64/128, at most 8192 rows and
+                                   not a small batch: the stream read, whose 1024
+                                   persistent waves each take an equal slice of
+                                   the batch's (kv head, row, position) stream, at
+                                   least 128 positions long (an explicit value
+                                   sets that minimum instead);
+                                 - bf16, head_dim 64/128, a small batch (at most
+                                   256 row x kv head pairs over a table of at
+                                   most 4096 positions, or any batch over a table
+                                   of at most 1024) or more than 8192 rows: the
+                                   matrix-core partition read, partitions of
+                                   cdiv(table, cdiv(256, rows x kv heads))
+                                   positions clamped to [768, 2048] and rounded
+                                   up to block_size (never longer than the table);
+                                 - fp32, and bf16 head_dim 16: the VALU partition
+                                   read, partitions of about 64 KiB of K and V
+                                   (65536 / (2 head_dim elem) positions: fp32 hd
+                                   64: 128, fp32 hd 128: 64, fp32 hd 16: 512, bf16
+                                   hd 16: 1024), rounded down to block_size and
+                                   never longer than the table */
 } pkv_attn_desc;
 
 /*
@@ -153,11 +181,18 @@ int pkv_paged_attention(const pkv_attn_desc *d, const void *q, const void *k_poo
                         const int32_t *context_lens, float scale, void *out,
                         void *workspace, size_t workspace_bytes, void *stream);
 
-/* Workspace bytes pkv_paged_attention needs for `d`: per row, query head and
- * partition, fp32 partial sums of head_dim values plus the running max and
- * sum.  0 when no row can span more than one partition.  Returns 0 for a
- * NULL descriptor. */
+/* Workspace bytes pkv_paged_attention needs for `d` (0 for a NULL or invalid
+ * descriptor, and for rows == 0).
+ *   - The stream read (see partition_tokens): always non-zero.  4-byte words:
+ *     a 4-word header, 2048 words of wave starts, rows + 1 group prefixes
+ *     (aligned to 4), then two partial slots per persistent wave (1024 waves)
+ *     of align4(G * (head_dim + 2)) fp32 values, G = n_heads / n_kv_heads --
+ *     whatever the table width: 4.3 MB for G = 4, head_dim 128.
+ *   - The partition reads: per row, query head and partition, fp32 partial
+ *     sums of head_dim values plus the running max and sum; 0 when one
+ *     partition covers the table. */
 size_t pkv_paged_attention_workspace_size(const pkv_attn_desc *d);
+
 
 /*
  * pkv_paged_attention_multi -- the paged read for a chunk of query_len
@@ -254,8 +289,21 @@ int pkv_read_stats_init(pkv_read_stats *s, int32_t mode, int32_t block);
 /* Count one read of the given shape (all >= 0); PKV_ERR_SHAPE on overflow. */
 int pkv_read_stats_record(pkv_read_stats *s, int32_t rows, int32_t heads, int32_t query_len,
                           int32_t width);
-/* Count one pkv_paged_attention call of descriptor d: one query per row, the
- * table's width max_blocks_per_row * block_size as the context width. */
+/* Positions of one (row, head) whose scores a workgroup of the library's read
+ * of `d` holds at once: 32 on the stream read (one wave, one 32-position
+ * group), 128 on the matrix-core partition read (four waves of one group
+ * each), 1024 * (16 / elem) / head_dim on the VALU partition read (four
+ * waves, each scoring four 16-byte-per-lane loads' worth of positions; fp32
+ * hd 64: 64, fp32 hd 128: 32, fp32 hd 16: 256, bf16 hd 16: 512); elem is
+ * the dtype's size in bytes.  0 for an invalid `d`.  A row cut into
+ * partitions holds one such tile per partition. */
+int32_t pkv_read_tile(const pkv_attn_desc *d);
+/* Count one pkv_paged_attention call of descriptor d on a streamed counter
+ * whose block is pkv_read_tile(d) (else PKV_ERR_MODE: the counter is of
+ * another read), or on a gathered counter: one query per row.  The library
+ * never reads the lengths, so the context width charged is the table's,
+ * max_blocks_per_row * block_size, an upper bound of the longest row; a
+ * caller that knows the longest row counts it with pkv_read_stats_record. */
 int pkv_read_stats_record_read(pkv_read_stats *s, const pkv_attn_desc *d);
 /* window = now - earlier; PKV_ERR_MODE if the two readings are of reads with
  * a different mode or block, PKV_ERR_SHAPE if `earlier` is not earlier. */

@@ -6,7 +6,7 @@ marshals torch tensors into pointers and a HIP stream.  The library is loaded
 on first use, and a missing library is an error: there is no fallback path.
 """
 from .binding import (  # noqa: F401
-    BlockAllocator, KVCacheExhausted, PkvError, ReadCounters, decode_step, reshape_and_cache, paged_attention, paged_attention_into,
-    paged_attention_multi, workspace_size_multi,
-    workspace_size, library_path, load_library,
+    BlockAllocator, KVCacheExhausted, PkvError, ReadCounters, decode_step, library_path, load_library,
+    paged_attention, paged_attention_into, paged_attention_multi, read_tile,
+    reshape_and_cache, workspace_size, workspace_size_multi,
 )

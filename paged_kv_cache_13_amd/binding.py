@@ -100,6 +100,8 @@ def load_library():
     lib.pkv_read_stats_record.restype = ctypes.c_int
     lib.pkv_read_stats_record_read.argtypes = [rs, ctypes.POINTER(AttnDesc)]
     lib.pkv_read_stats_record_read.restype = ctypes.c_int
+    lib.pkv_read_tile.argtypes = [ctypes.POINTER(AttnDesc)]
+    lib.pkv_read_tile.restype = i32
     lib.pkv_read_stats_since.argtypes = [rs, rs, rs]
     lib.pkv_read_stats_since.restype = ctypes.c_int
     lib.pkv_read_stats_saving.argtypes = [rs]
@@ -220,6 +222,14 @@ def paged_attention_into(q, k_pool, v_pool, block_table, context_lens, scale, ou
     if stats is not None:
         stats.record_read(d)
     return out
+
+
+def read_tile(q: torch.Tensor, k_pool: torch.Tensor, block_table: torch.Tensor,
+              out_dtype: Optional[torch.dtype] = None, partition_tokens: int = 0) -> int:
+    """Positions of one (row, head) whose scores a workgroup of the library's
+    read of these shapes holds at once (pkv_read_tile)."""
+    d = _desc(q, k_pool, block_table, _DTYPES[out_dtype or q.dtype], partition_tokens)
+    return int(load_library().pkv_read_tile(ctypes.byref(d)))
 
 
 def workspace_size_multi(q: torch.Tensor, k_pool: torch.Tensor, block_table: torch.Tensor,

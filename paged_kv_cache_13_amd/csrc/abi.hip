@@ -144,9 +144,7 @@ int plan_decode(const pkv_attn_desc *d, Plan *pl) {
     pl->cg_min = d->partition_tokens ? (part + pkv::kGroupPositions - 1) / pkv::kGroupPositions
                                      : kStreamMinGroups;
     pl->max_parts = (int32_t)((cap_groups + pl->cg_min - 1) / pl->cg_min + 1);
-    if (d->rows > 0)
-      pl->ws_bytes = pkv::stream_layout(d->rows, d->n_kv_heads, pl->group, d->head_dim, pl->max_parts).total *
-                     sizeof(int32_t);
+    if (d->rows > 0) pl->ws_bytes = pkv::stream_layout(d->rows, pl->group, d->head_dim).total * sizeof(int32_t);
     return PKV_OK;
   }
   pl->cg_min = 0;
@@ -199,9 +197,8 @@ int plan_multi(const pkv_attn_desc *d, int32_t query_len, Plan *pl, MultiPlan *m
                (int64_t)d->rows * d->n_kv_heads * cap_groups >= kStreamMultiGroups * pkv::kStreamWaves;
   if (mp->stream) {
     mp->q_tiles = mp->q_per_tile = mp->q_blocks = 0;
-    pl->ws_bytes = d->rows > 0 ? pkv::stream_layout(d->rows, d->n_kv_heads, query_len * pl->group, d->head_dim,
-                                                    pl->max_parts).total * sizeof(int32_t)
-                               : 0;
+    pl->ws_bytes =
+        d->rows > 0 ? pkv::stream_layout(d->rows, query_len * pl->group, d->head_dim).total * sizeof(int32_t) : 0;
     return PKV_OK;
   }
   const int32_t cap = d->max_blocks_per_row * d->block_size;
@@ -244,15 +241,22 @@ int check_scatter(const void *k, const void *v, const int64_t *slot_mapping, int
                   int32_t n_kv_heads, int32_t head_dim, int32_t dtype);
 
 // Every host-side check of a read, before anything is enqueued.
-int check_attention(const pkv_attn_desc *d, const void *q, const void *k_pool, const void *v_pool,
-                    const int32_t *block_table, const int32_t *context_lens, const void *out,
-                    const void *workspace, size_t workspace_bytes, Plan *pl) {
+int check_attention_args(const pkv_attn_desc *d, const void *q, const void *k_pool, const void *v_pool,
+                         const int32_t *block_table, const int32_t *context_lens, const void *out, Plan *pl) {
   const int st = plan_decode(d, pl);
   if (st != PKV_OK) return st;
   if (!q || !k_pool || !v_pool || !block_table || !context_lens || !out) return PKV_ERR_NULL;
   if (!aligned(q, 16) || !aligned(k_pool, 16) || !aligned(v_pool, 16) || !aligned(out, 16) ||
       !aligned(block_table, 4) || !aligned(context_lens, 4))
     return PKV_ERR_ALIGN;
+  return PKV_OK;
+}
+
+int check_attention(const pkv_attn_desc *d, const void *q, const void *k_pool, const void *v_pool,
+                    const int32_t *block_table, const int32_t *context_lens, const void *out,
+                    const void *workspace, size_t workspace_bytes, Plan *pl) {
+  const int st = check_attention_args(d, q, k_pool, v_pool, block_table, context_lens, out, pl);
+  if (st != PKV_OK) return st;
   if (pl->ws_bytes > 0) {
     if (!workspace || workspace_bytes < pl->ws_bytes) return PKV_ERR_WORKSPACE;
     if (!aligned(workspace, 16)) return PKV_ERR_ALIGN;
@@ -303,7 +307,7 @@ int launch_attention(const pkv_attn_desc *d, const Plan &pl, const void *q, cons
 
 extern "C" {
 
-int pkv_version(void) { return 200; }
+int pkv_version(void) { return 300; }
 
 const char *pkv_strerror(int status) {
   switch (status) {
@@ -379,6 +383,7 @@ int pkv_paged_attention(const pkv_attn_desc *d, const void *q, const void *k_poo
   return launch_attention(d, pl, q, k_pool, v_pool, block_table, context_lens, scale, out, workspace,
                           static_cast<hipStream_t>(stream));
 }
+
 
 size_t pkv_paged_attention_multi_workspace_size(const pkv_attn_desc *d, int32_t query_len) {
   Plan pl;
@@ -508,11 +513,22 @@ int pkv_read_stats_record(pkv_read_stats *s, int32_t rows, int32_t heads, int32_
   return PKV_OK;
 }
 
+int32_t pkv_read_tile(const pkv_attn_desc *d) {
+  Plan pl;
+  if (plan_decode(d, &pl) != PKV_OK) return 0;
+  if (pl.stream) return pkv::kGroupPositions;  // one wave, one group
+  if (d->dtype == PKV_BF16 && (d->head_dim == 64 || d->head_dim == 128))
+    return 4 * pkv::kGroupPositions;  // decode_partition_mfma: four waves, one group each
+  // decode_partition: four waves x four 16-byte loads per lane, each load
+  // covering 64 / (head_dim / (16 / elem)) positions
+  return (int32_t)(1024 * (16 / elem_bytes(d->dtype)) / d->head_dim);
+}
+
 int pkv_read_stats_record_read(pkv_read_stats *s, const pkv_attn_desc *d) {
   if (!s || !d) return PKV_ERR_NULL;
-  if (d->rows < 0 || d->n_heads < 1 || d->max_blocks_per_row < 1 || d->block_size < 1 ||
-      (int64_t)d->max_blocks_per_row * d->block_size > INT_MAX)
-    return PKV_ERR_SHAPE;
+  const int32_t tile = pkv_read_tile(d);
+  if (tile == 0 || d->rows < 0) return PKV_ERR_SHAPE;
+  if (s->mode == PKV_READ_STREAMED && s->block != tile) return PKV_ERR_MODE;
   return pkv_read_stats_record(s, d->rows, d->n_heads, 1, d->max_blocks_per_row * d->block_size);
 }
 

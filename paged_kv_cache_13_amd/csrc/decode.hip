@@ -891,7 +891,7 @@ __global__ __launch_bounds__(1024) void decode_plan(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int rows = a.rows;
   const int cap = a.max_blocks_per_row * a.block_size;
-  const StreamLayout L = stream_layout(rows, a.n_kv_heads, a.cols, a.head_dim, a.max_parts);
+  const StreamLayout L = stream_layout(rows, a.cols, a.head_dim);
   int32_t *wsi = reinterpret_cast<int32_t *>(a.ws);
   const int per = (rows + 1023) / 1024;
   const int r0 = min(rows, tid * per), r1 = min(rows, r0 + per);
@@ -1183,7 +1183,7 @@ __device__ __forceinline__ void write_out_rows(const DecodeArgs &a, const Cursor
 // into several slices, this slice's partial (max, sum, rescaled acc) for
 // decode_stream_merge.  Plain stores: the merge runs as the next kernel.
 template <int HD>
-__device__ __forceinline__ void segment_end(const DecodeArgs &a, const StreamLayout &L, const Cursor &c,
+__device__ __forceinline__ void segment_end(const DecodeArgs &a, const StreamLayout &L, const Cursor &c, int w,
                                             f32x4_t *acc, float &m, float &l, int lr, int lg) {
   constexpr int DT = HD / 16;
   const int C = a.cols;
@@ -1191,8 +1191,8 @@ __device__ __forceinline__ void segment_end(const DecodeArgs &a, const StreamLay
   if (c.nparts == 1) {
     if (lr < C) write_out_rows<HD>(a, c, acc, lt > 0.f ? 1.f / lt : 0.f, lr, lg);  // 0: a query before the history
   } else if (lr < C) {
-    const size_t pair = (size_t)c.kvh * a.rows + c.r;
-    float *slot = a.ws + L.partials + (pair * a.max_parts + c.part) * L.slot_stride;
+    // piece c.part of the pair: 2w + 1 for its first piece, 2w for a later one
+    float *slot = a.ws + L.partials + (size_t)(c.part == 0 ? 2 * w + 1 : 2 * w) * L.slot_stride;
 #pragma unroll
     for (int dt = 0; dt < DT; ++dt) *reinterpret_cast<f32x4_t *>(slot + lr * HD + 16 * dt + 4 * lg) = acc[dt];
     if (lg == 0) {
@@ -1214,7 +1214,7 @@ __device__ __forceinline__ void segment_end(const DecodeArgs &a, const StreamLay
 constexpr int kMergeMaxParts = 8;
 constexpr int kMergeElems = 2;
 __global__ __launch_bounds__(256) void decode_stream_merge(DecodeArgs a) {
-  const StreamLayout L = stream_layout(a.rows, a.n_kv_heads, a.cols, a.head_dim, a.max_parts);
+  const StreamLayout L = stream_layout(a.rows, a.cols, a.head_dim);
   const int32_t *wsi = reinterpret_cast<const int32_t *>(a.ws);
   const int pair = blockIdx.x;
   const int kvh = pair / a.rows, r = pair - kvh * a.rows;
@@ -1257,10 +1257,11 @@ __global__ __launch_bounds__(256) void decode_stream_merge(DecodeArgs a) {
   if (ng == 0) return;
   const long long ng_all = (long long)a.n_kv_heads * ngk;
   const long long S = (long long)kvh * ngk + g0;
-  const int nparts = (int)(slice_of(S + ng - 1, ng_all, waves) - slice_of(S, ng_all, waves) + 1);
+  const long long first = slice_of(S, ng_all, waves);
+  const int nparts = (int)(slice_of(S + ng - 1, ng_all, waves) - first + 1);
   if (nparts <= 1) return;
   const int C = a.cols, HD = a.head_dim;
-  const float *slots = a.ws + L.partials + (size_t)pair * a.max_parts * L.slot_stride;
+  const float *parts = a.ws + L.partials;
   // Each thread merges kMergeElems outputs at a time, every partial load of
   // them issued before any output is stored (a store in between would keep
   // the next loads behind it: the compiler cannot tell out from the
@@ -1279,7 +1280,7 @@ __global__ __launch_bounds__(256) void decode_stream_merge(DecodeArgs a) {
 #pragma unroll
         for (int k = 0; k < kMergeMaxParts; ++k) {
           if (idx < C * HD && k < kn) {
-            const float *sk = slots + (size_t)(k0 + k) * L.slot_stride;
+            const float *sk = parts + stream_piece_slot(first, k0 + k) * L.slot_stride;
             mk[e][k] = sk[C * HD + j];
             lk[e][k] = sk[C * HD + C + j];
             ak[e][k] = sk[j * HD + d];
@@ -1396,7 +1397,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
   __shared__ uint4 s_k[2 * KS * kWave];
   __shared__ uint4 s_v[DT * kWave];
   __shared__ int32_t s_wctx[kWindowRows], s_wgpre[kWindowRows];
-  const StreamLayout L = stream_layout(a.rows, a.n_kv_heads, a.cols, a.head_dim, a.max_parts);
+  const StreamLayout L = stream_layout(a.rows, a.cols, a.head_dim);
   const int32_t *wsi = reinterpret_cast<const int32_t *>(a.ws);
   const int w = blockIdx.x;
   const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
@@ -1500,7 +1501,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
     // causal inside a chunk: query qcol sees positions below n - query_len + qcol + 1
     const int cend = max(c0.n - a.query_len + qcol + 1, 0);
     group_softmax_pv<HD>(sacc, vc, acc, m, l, cscale, cend, c0.n, c0.j * kGroupPositions, lg);
-    if (c0.j == c0.ng - 1 || last_group) segment_end<HD>(a, L, c0, acc, m, l, lr, lg);
+    if (c0.j == c0.ng - 1 || last_group) segment_end<HD>(a, L, c0, w, acc, m, l, lr, lg);
     if (last_group) break;
     const bool new_row = c1.r != c0.r || c1.kvh != c0.kvh;
     c0 = c1;

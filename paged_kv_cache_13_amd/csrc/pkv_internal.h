@@ -71,10 +71,20 @@ __host__ __device__ inline WsLayout ws_layout(int32_t rows, int32_t n_heads, int
 //   hdr[4]                 groups per kv head, waves used, two words unused
 //   first_pos[2 * waves]   (kv head * rows + row, group) where each wave starts
 //   gpre[rows + 1]         exclusive prefix of groups per row
-//   partials[kv * rows * max_parts][slot]  fp32 acc[cols][hd], m[cols], l[cols]
+//   partials[2 * kStreamWaves][slot]  fp32 acc[cols][hd], m[cols], l[cols]
 // The plan words (hdr, first_pos, gpre) are written by decode_plan; a batch
 // of at most kWindowRows rows is planned inside every wave and leaves them
 // unused.
+//
+// Partial slots belong to waves, not to (kv head, row) pairs.  Inside one
+// wave's slice only the first and the last segment can be pieces of a pair
+// cut by a slice boundary (every segment in between is a whole pair, which
+// the wave writes to `out` itself).  A cut pair's first piece is the last
+// segment of the slice it starts in, and each later piece is the first
+// segment of the next slices.  So a wave owns two slots: 2w + 1 for a piece
+// that starts a cut pair, 2w for a later piece; a pair whose first piece is
+// in slice f keeps piece k at stream_piece_slot(f, k).  The workspace grows
+// with the number of waves, not with the table width.
 constexpr int kStreamWaves = 1024;  // one persistent wave per SIMD (4 per CU)
 constexpr int kWindowRows = 256;  // rows a wave keeps (and, if that is all, plans) in LDS
 constexpr int kPlanMaxRows = 8192;
@@ -84,16 +94,19 @@ struct StreamLayout {
   size_t slot_stride;
 };
 __host__ __device__ inline size_t align4(size_t x) { return (x + 3) & ~(size_t)3; }
-__host__ __device__ inline StreamLayout stream_layout(int32_t rows, int32_t n_kv, int32_t cols,
-                                                      int32_t head_dim, int32_t max_parts) {
+__host__ __device__ inline StreamLayout stream_layout(int32_t rows, int32_t cols, int32_t head_dim) {
   StreamLayout L;
   L.hdr = 0;
   L.first_pos = 4;
   L.gpre = L.first_pos + 2 * (size_t)kStreamWaves;
   L.partials = align4(L.gpre + (size_t)rows + 1);
   L.slot_stride = align4((size_t)cols * (head_dim + 2));
-  L.total = L.partials + (size_t)n_kv * rows * max_parts * L.slot_stride;
+  L.total = L.partials + 2 * (size_t)kStreamWaves * L.slot_stride;
   return L;
+}
+// Slot of piece k of a cut pair whose first piece lies in slice `first`.
+__host__ __device__ inline size_t stream_piece_slot(long long first, int k) {
+  return k == 0 ? (size_t)(2 * first + 1) : (size_t)(2 * (first + k));
 }
 
 hipError_t launch_decode(const DecodeArgs &a, hipStream_t stream);

@@ -36,7 +36,7 @@ def test_header_declares_the_entry_points():
                                     "pkv_paged_attention_multi", "pkv_paged_attention_multi_workspace_size",
                                     "pkv_paged_attention_workspace_size", "pkv_read_stats_init",
                                     "pkv_read_stats_record", "pkv_read_stats_record_read",
-                                    "pkv_read_stats_saving", "pkv_read_stats_since",
+                                    "pkv_read_stats_saving", "pkv_read_stats_since", "pkv_read_tile",
                                     "pkv_reshape_and_cache", "pkv_strerror", "pkv_version"]
 
 
@@ -50,7 +50,7 @@ def test_status_strings(lib):
         assert lib.pkv_strerror(code).decode() != "unknown status"
     assert lib.pkv_strerror(0).decode() == "ok"
     assert lib.pkv_strerror(999).decode() == "unknown status"
-    assert lib.pkv_version() == 200
+    assert lib.pkv_version() == 300
 
 
 def desc(**kw):
@@ -88,17 +88,20 @@ def test_workspace_size_partition_layout(lib):
 
 def test_workspace_size_stream_layout(lib):
     # bf16, head_dim 128: header (4 words), 1024 wave starts (2 words each),
-    # 65 group prefixes, aligned; then per (kv head, row)
-    # one partial slot of align4(4 heads x 130) = 520 floats per slice that can
-    # cut it: the default slices hold at least 4 groups of 32 positions, so
-    # 128 / 4 + 1 = 33 slots
+    # 65 group prefixes, aligned; then two partial slots per persistent wave
+    # (a piece that starts a cut (kv head, row) and a later piece), each of
+    # align4(4 heads x 130) = 520 floats, whatever the table width
     head = 4 + 2 * 1024 + 65
     head += -head % 4
-    assert ws(lib) == (head + 8 * 64 * 33 * 520) * 4
-    # an explicit partition length sets the minimum slice: 512 -> 16 groups
-    assert ws(lib, partition_tokens=512) == (head + 8 * 64 * 9 * 520) * 4
-    # the stream layout always needs its header, even when no row can split
-    assert ws(lib, partition_tokens=4096) == (head + 8 * 64 * 2 * 520) * 4
+    assert ws(lib) == (head + 2 * 1024 * 520) * 4
+    # the slice length does not change the slots a wave owns
+    assert ws(lib, partition_tokens=512) == (head + 2 * 1024 * 520) * 4
+    # the stream layout always needs its header and slots, even when no row can split
+    assert ws(lib, partition_tokens=4096) == (head + 2 * 1024 * 520) * 4
+    # a 32768-position table: the same slots (256 rows: 257 group prefixes)
+    head256 = 4 + 2 * 1024 + 257
+    head256 += -head256 % 4
+    assert ws(lib, rows=256, block_size=32, max_blocks_per_row=1024) == (head256 + 2 * 1024 * 520) * 4
     # more rows than the plan kernel scans: back to partitions
     assert ws(lib, rows=9000, max_blocks_per_row=32) == 0
 
@@ -124,6 +127,32 @@ def test_small_batches_over_short_tables_take_partitions(lib):
     assert ws(lib, rows=32, max_blocks_per_row=257) != part(rows=32, max_blocks_per_row=257)
     assert ws(lib, rows=33) != part(rows=33)
     assert ws(lib, rows=33) > 4 * (2 * 1024)  # the stream header is there
+
+
+def test_default_partitions_stated_in_the_header(lib):
+    # pkv.h, pkv_attn_desc.partition_tokens: each path's default, checked
+    # through the workspace it implies (m, l and head_dim partial sums per
+    # (row, head, partition); 0 when one partition covers the table)
+    def part_ws(rows, heads, parts, hd):
+        slots = rows * heads * parts
+        return 0 if parts <= 1 else (((2 * slots + 3) & ~3) + slots * hd) * 4
+    # matrix-core partition read: cdiv(table, cdiv(256, rows x kv heads)),
+    # clamped to [768, 2048]
+    assert ws(lib, rows=16) == part_ws(16, 32, 2, 128)                          # 4096 / 2 = 2048
+    assert ws(lib, rows=4) == part_ws(4, 32, 6, 128)                            # 4096 / 8 -> 768
+    assert ws(lib, rows=8, max_blocks_per_row=64) == part_ws(8, 32, 2, 128)     # 1024 / 4 -> 768
+    assert ws(lib, rows=64, max_blocks_per_row=48) == 0                         # 768: one partition
+    assert ws(lib, rows=9000) == part_ws(9000, 32, 2, 128)                      # > 8192 rows: 4096 -> 2048
+    # VALU partition read: about 64 KiB of K and V per partition
+    f32 = dict(dtype=0, out_dtype=0)
+    assert ws(lib, rows=8, n_heads=8, n_kv_heads=2, head_dim=64, max_blocks_per_row=64, **f32) == \
+        part_ws(8, 8, 8, 64)                                                    # 128 positions
+    assert ws(lib, head_dim=128, **f32) == part_ws(64, 32, 64, 128)             # 64 positions
+    assert ws(lib, head_dim=16, block_size=8, max_blocks_per_row=256, **f32) == \
+        part_ws(64, 32, 4, 16)                                                  # 512 positions
+    assert ws(lib, head_dim=16) == part_ws(64, 32, 4, 16)                       # bf16 hd 16: 1024
+    # the stream read: header and two slots per wave, whatever the slice minimum
+    assert ws(lib) == ws(lib, partition_tokens=1024) > 0
 
 
 def attn(lib, d, q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, cl=FAKE, out=FAKE, wsp=FAKE, wsb=1 << 40):
@@ -247,11 +276,32 @@ def test_read_counters_window_and_refusals(lib):
     assert g.calls == 1
 
 
+def test_read_tile_names_what_each_read_holds(lib):
+    tile = lambda **kw: lib.pkv_read_tile(ctypes.byref(desc(**kw)))
+    assert tile() == 32                                   # stream read: one wave, one group
+    assert tile(rows=8, max_blocks_per_row=64) == 128     # matrix-core partition read
+    assert tile(dtype=0, out_dtype=0, head_dim=64) == 64  # VALU partition read, fp32
+    assert tile(dtype=0, out_dtype=0, head_dim=128) == 32
+    assert tile(dtype=0, out_dtype=0, head_dim=16) == 256
+    assert tile(head_dim=16) == 512                       # bf16 head_dim 16: VALU
+    assert tile(head_dim=96) == 0
+    assert lib.pkv_read_tile(None) == 0
+
+
 def test_read_counters_count_a_descriptor(lib):
-    c = binding.ReadCounters("streamed", 16)
     d = desc(rows=64, n_heads=32, max_blocks_per_row=256, block_size=16)
+    c = binding.ReadCounters("streamed", lib.pkv_read_tile(ctypes.byref(d)))
     c.record_read(d)
-    assert (c.calls, c.rows, c.score_cells, c.held_cells) == (1, 64, 64 * 32 * 4096, 64 * 32 * 16)
+    # the table's width is charged (the library never reads the lengths);
+    # the stream read holds 32 positions per (row, head)
+    assert (c.calls, c.rows, c.score_cells, c.held_cells) == (1, 64, 64 * 32 * 4096, 64 * 32 * 32)
+    # a streamed counter of another tile width is another read's counter
+    with pytest.raises(binding.PkvError) as e:
+        binding.ReadCounters("streamed", 16).record_read(d)
+    assert e.value.status == 11
+    g = binding.ReadCounters("gathered", 1)
+    g.record_read(d)
+    assert g.held_cells == g.score_cells == 64 * 32 * 4096
 
 
 # ---------------------------------------------------------------------------
@@ -276,12 +326,12 @@ def test_multi_query_workspace(lib):
     ws = lambda d, q: lib.pkv_paged_attention_multi_workspace_size(ctypes.byref(d), q)
     # 4 queries x 4 heads per kv head = 16 columns: the stream path, whose
     # workspace is the one-query read's layout with 16 columns per slot --
-    # header, wave starts, row prefixes, then 33 slices (4-group
-    # minimum over a 128-group table) per (kv head, row) of 16 x (128 + 2)
+    # header, wave starts, row prefixes, then two slots per persistent wave
+    # of 16 x (128 + 2) floats
     d = desc()
     head = 4 + 2 * 1024 + 65
     head = (head + 3) & ~3
-    assert ws(d, 4) == (head + 8 * 64 * 33 * 16 * 130) * 4
+    assert ws(d, 4) == (head + 2 * 1024 * 16 * 130) * 4
     # 8 queries (32 columns): the workgroup path.  64 rows x 8 kv heads x one
     # query block (a two-wave workgroup, two per compute unit) = 512 blocks
     # on 512 slots: a 4096-position table wants 4096-position partitions,

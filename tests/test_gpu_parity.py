@@ -288,8 +288,9 @@ def test_decode_run_sweep(rows, bs):
     k, v, slots = run.prefill()
     pkv.reshape_and_cache(k, v, slots, run.k_pool, run.v_pool)
     check_oracle = {0, steps // 2, steps - 1}
-    stats = pkv.ReadCounters("streamed", block=bs)
     out = torch.empty(rows, run.n_heads, run.head_dim, dtype=torch.bfloat16, device=DEV)
+    tile = pkv.read_tile(out, run.k_pool, run.block_table())  # the read's own tile, not the pool block
+    stats = pkv.ReadCounters("streamed", block=tile)
     for step in range(steps):
         q, kn, vn, sl = run.step()
         pkv.reshape_and_cache(kn, vn, sl, run.k_pool, run.v_pool)
@@ -307,9 +308,9 @@ def test_decode_run_sweep(rows, bs):
             assert_close(out.float().cpu()[torch.as_tensor(sample)], ref, what="step %d vs oracle" % step,
                          **TOL[torch.bfloat16])
     assert list(np.unique(run.ctx_host)) == [512 + steps]
-    # run saving: sum of widths over sum of held tiles
+    # run saving: sum of widths (the longest row of each step) over sum of held tiles
     widths = np.arange(513, 513 + steps)
-    assert stats.saving == pytest.approx(widths.sum() / np.minimum(bs, widths).sum())
+    assert stats.saving == pytest.approx(widths.sum() / np.minimum(tile, widths).sum())
 
 
 # ---------------------------------------------------------------------------
@@ -382,7 +383,7 @@ def test_decode_step_replays_from_a_graph(rows, prompt):
     s_q, s_kn, s_vn, s_sl, s_bt, s_cl = [t.clone() for t in (q, kn, vn, sl, bt, cl)]
     s_out = torch.empty_like(q)
     ws = torch.zeros(max(pkv.workspace_size(q, run.k_pool, bt), 1), dtype=torch.uint8, device=DEV)
-    counters = pkv.ReadCounters("streamed", block=bs)
+    counters = pkv.ReadCounters("streamed", block=pkv.read_tile(q, run.k_pool, bt))
     side = torch.cuda.Stream()
     side.wait_stream(torch.cuda.current_stream())
     with torch.cuda.stream(side):  # warm-up outside the capture, on a scratch copy of the pools
@@ -491,10 +492,10 @@ def test_read_many_rows(rows, width):
 
 @pytest.mark.parametrize("name", ["llama3_8b_layer", "skewed_long"])
 def test_stream_read_ignores_stale_workspace(name):
-    # a row cut into several slices is merged by the slice that arrives last
-    # on the row's arrival word, which carries the dispatch's tag: whatever
-    # the workspace holds beforehand (zeros, all ones, random bytes, the words
-    # of a read of other lengths, on this stream or another), the bits agree
+    # every plan word and partial slot the merge kernel reads is written
+    # earlier in the same call, so whatever the workspace holds beforehand
+    # (zeros, all ones, random bytes, the words of a read of other lengths,
+    # on this stream or another), the bits agree
     b = synth.make_batch(synth.CONFIGS[name], device=DEV)
     other = synth.make_batch(synth.CONFIGS[name], device=DEV, seed=synth.CONFIGS[name].seed + 11)
     n = max(pkv.workspace_size(b.q, b.k_pool, b.block_table), pkv.workspace_size(other.q, other.k_pool,
@@ -527,8 +528,8 @@ def test_stream_read_ignores_stale_workspace(name):
 @pytest.mark.parametrize("rows,KV,ctx", [(1, 1, 32768), (2, 2, 20000), (3, 8, 4097)])
 def test_read_row_cut_into_many_slices(rows, KV, ctx):
     # few (kv head, row) pairs over long tables: each pair is cut into up to
-    # hundreds of slices, all counting on one arrival word, and merged in
-    # batches of slices
+    # hundreds of slices, whose partials the merge kernel combines in
+    # batches of eight
     cfg = synth.DecodeConfig("many_slices", "bf16", rows=rows, n_heads=4 * KV, n_kv_heads=KV, head_dim=128,
                              block_size=16, ctx=("fixed", tuple([ctx] * rows)), pool=("factor", 1.0),
                              max_ctx=ctx, value_scale=0.5, seed=rows * 7 + KV)
