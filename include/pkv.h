@@ -44,8 +44,10 @@
  *
  * Ownership: the caller owns every buffer, the workspace included; the
  * library allocates no device memory, keeps no state between calls and is
- * reentrant.  Every call enqueues its kernels on `stream` (a hipStream_t,
- * NULL = the default stream) and returns without waiting for them.
+ * reentrant -- except pkv_paged_attention_noalloc, whose static scratch buffer
+ * is loaded with the library's code on each GPU and shared by its calls.
+ * Every call enqueues its kernels on `stream` (a hipStream_t, NULL = the
+ * default stream) and returns without waiting for them.
  *
  * Errors: every entry point returns a pkv_status and never aborts.  Shapes,
  * pointers, alignment, dtypes and the workspace size are checked on the host
@@ -79,7 +81,9 @@ typedef enum pkv_status {
   PKV_ERR_PARTITION = 9,     /* partition_tokens not a positive multiple of block_size */
   PKV_ERR_LAUNCH = 10,       /* the HIP runtime refused a launch (hipGetLastError) */
   PKV_ERR_MODE = 11,         /* read counters of different reads (mode or block differ) */
-  PKV_ERR_EXHAUSTED = 12     /* the pool has fewer free blocks than asked for */
+  PKV_ERR_EXHAUSTED = 12,    /* the pool has fewer free blocks than asked for */
+  PKV_ERR_SCRATCH = 13       /* pkv_paged_attention_noalloc: the read needs more scratch
+                                than PKV_NOALLOC_SCRATCH_BYTES */
 } pkv_status;
 
 typedef enum pkv_dtype {
@@ -193,6 +197,26 @@ int pkv_paged_attention(const pkv_attn_desc *d, const void *q, const void *k_poo
  *     partition covers the table. */
 size_t pkv_paged_attention_workspace_size(const pkv_attn_desc *d);
 
+/*
+ * pkv_paged_attention_noalloc -- pkv_paged_attention for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, results and errors,
+ * bit for bit the same output, minus the workspace: the read keeps its
+ * partial slots and plan words in a static device buffer of
+ * PKV_NOALLOC_SCRATCH_BYTES that the library holds on every GPU it runs on
+ * until the process ends.  No device memory is allocated or freed by the
+ * call.  A read whose pkv_paged_attention_workspace_size exceeds that size is
+ * refused with PKV_ERR_SCRATCH before anything is enqueued.  The buffer is
+ * looked up on the first call made with a device current, so `stream` must
+ * belong to the current device.  Every call on one GPU shares that GPU's
+ * buffer: two calls whose work overlaps on one GPU (another stream, or
+ * another thread) race and return garbage; calls in order on one stream do
+ * not.  The buffer keeps the last call's contents; no call needs it zeroed.
+ */
+#define PKV_NOALLOC_SCRATCH_BYTES (32u << 20)
+int pkv_paged_attention_noalloc(const pkv_attn_desc *d, const void *q, const void *k_pool,
+                                const void *v_pool, const int32_t *block_table,
+                                const int32_t *context_lens, float scale, void *out, void *stream);
 
 /*
  * pkv_paged_attention_multi -- the paged read for a chunk of query_len

@@ -7,6 +7,6 @@ on first use, and a missing library is an error: there is no fallback path.
 """
 from .binding import (  # noqa: F401
     BlockAllocator, KVCacheExhausted, PkvError, ReadCounters, decode_step, library_path, load_library,
-    paged_attention, paged_attention_into, paged_attention_multi, read_tile,
+    paged_attention, paged_attention_into, paged_attention_multi, paged_attention_noalloc, read_tile,
     reshape_and_cache, workspace_size, workspace_size_multi,
 )

@@ -102,6 +102,9 @@ def load_library():
     lib.pkv_read_stats_record_read.restype = ctypes.c_int
     lib.pkv_read_tile.argtypes = [ctypes.POINTER(AttnDesc)]
     lib.pkv_read_tile.restype = i32
+    lib.pkv_paged_attention_noalloc.argtypes = [ctypes.POINTER(AttnDesc), vp, vp, vp, vp, vp,
+                                                ctypes.c_float, vp, vp]
+    lib.pkv_paged_attention_noalloc.restype = ctypes.c_int
     lib.pkv_read_stats_since.argtypes = [rs, rs, rs]
     lib.pkv_read_stats_since.restype = ctypes.c_int
     lib.pkv_read_stats_saving.argtypes = [rs]
@@ -230,6 +233,27 @@ def read_tile(q: torch.Tensor, k_pool: torch.Tensor, block_table: torch.Tensor,
     read of these shapes holds at once (pkv_read_tile)."""
     d = _desc(q, k_pool, block_table, _DTYPES[out_dtype or q.dtype], partition_tokens)
     return int(load_library().pkv_read_tile(ctypes.byref(d)))
+
+
+def paged_attention_noalloc(q, k_pool, v_pool, block_table, context_lens, scale, out,
+                            partition_tokens: int = 0) -> torch.Tensor:
+    """The paged decode read into `out` with no workspace argument and no
+    allocation: the library keeps its scratch in a static buffer of
+    PKV_NOALLOC_SCRATCH_BYTES per GPU (calls overlapping on one GPU race)."""
+    dev = _on_gpu(q, k_pool, v_pool, block_table, context_lens, out)
+    _require(q.dim() == 3, "q must be [rows, n_heads, head_dim]")
+    _check_pools(k_pool, v_pool)
+    _require(k_pool.dtype == q.dtype and v_pool.dtype == q.dtype, "q and pools must share one dtype")
+    _require(block_table.dtype == torch.int32 and block_table.dim() == 2
+             and block_table.shape[0] == q.shape[0], "block_table must be int32 [rows, max_blocks]")
+    _require(context_lens.dtype == torch.int32 and context_lens.shape == (q.shape[0],),
+             "context_lens must be int32 [rows]")
+    _require(out.shape == q.shape, "out must be [rows, n_heads, head_dim]")
+    d = _desc(q, k_pool, block_table, _dtype_code(out), partition_tokens)
+    _check(load_library().pkv_paged_attention_noalloc(
+        ctypes.byref(d), q.data_ptr(), k_pool.data_ptr(), v_pool.data_ptr(), block_table.data_ptr(),
+        context_lens.data_ptr(), ctypes.c_float(scale), out.data_ptr(), _stream_handle(dev)))
+    return out
 
 
 def workspace_size_multi(q: torch.Tensor, k_pool: torch.Tensor, block_table: torch.Tensor,

@@ -8,6 +8,7 @@
 #include <limits.h>
 
 #include <algorithm>
+#include <mutex>
 
 #include "pkv.h"
 #include "pkv_internal.h"
@@ -324,6 +325,7 @@ const char *pkv_strerror(int status) {
     case PKV_ERR_LAUNCH: return "the HIP runtime refused a kernel launch";
     case PKV_ERR_MODE: return "read counters of different reads (mode or block differ)";
     case PKV_ERR_EXHAUSTED: return "the pool has fewer free blocks than asked for";
+    case PKV_ERR_SCRATCH: return "the read needs more scratch than the library's static buffer holds";
     default: return "unknown status";
   }
 }
@@ -384,6 +386,62 @@ int pkv_paged_attention(const pkv_attn_desc *d, const void *q, const void *k_poo
                           static_cast<hipStream_t>(stream));
 }
 
+}  // extern "C"
+
+// ---------------------------------------------------------------------------
+// The read for callers that cannot allocate (HIP graph capture, tight serving
+// loops): its scratch -- the partial slots and plan words the kernels would
+// otherwise keep in the caller's workspace -- is this file-scope device
+// array.  Every GPU the library runs on holds its own copy from the module's
+// load until the process ends.  In host code `scratch` names a host-side
+// stand-in, never the device copy: host code only ever uses the address
+// hipGetSymbolAddress returns for the current device, kept per device below.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[PKV_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices];  // device address of `scratch` on each device, once looked up
+
+// Device address of `scratch` on the current device, looked up on the first
+// call made with that device current.
+int scratch_of_current_device(void **ptr) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return PKV_ERR_LAUNCH;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void *p = nullptr;
+    if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return PKV_ERR_LAUNCH;
+    g_scratch_ptr[dev] = p;
+  }
+  *ptr = g_scratch_ptr[dev];
+  return PKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int pkv_paged_attention_noalloc(const pkv_attn_desc *d, const void *q, const void *k_pool, const void *v_pool,
+                                const int32_t *block_table, const int32_t *context_lens, float scale, void *out,
+                                void *stream) {
+  Plan pl;
+  int st = check_attention_args(d, q, k_pool, v_pool, block_table, context_lens, out, &pl);
+  if (st != PKV_OK) return st;
+  if (pl.ws_bytes > (size_t)PKV_NOALLOC_SCRATCH_BYTES) return PKV_ERR_SCRATCH;
+  if (d->rows == 0) return PKV_OK;
+  void *ws = nullptr;
+  if (pl.ws_bytes > 0) {
+    st = scratch_of_current_device(&ws);
+    if (st != PKV_OK) return st;
+  }
+  // The kernels need no zeroed scratch: every partial slot and plan word a
+  // call reads is written earlier in the same call.
+  return launch_attention(d, pl, q, k_pool, v_pool, block_table, context_lens, scale, out, ws,
+                          static_cast<hipStream_t>(stream));
+}
 
 size_t pkv_paged_attention_multi_workspace_size(const pkv_attn_desc *d, int32_t query_len) {
   Plan pl;

@@ -34,6 +34,7 @@ def test_header_declares_the_entry_points():
                                     "pkv_allocator_num_free", "pkv_allocator_storage_bytes",
                                     "pkv_append_slots", "pkv_decode_step", "pkv_paged_attention",
                                     "pkv_paged_attention_multi", "pkv_paged_attention_multi_workspace_size",
+                                    "pkv_paged_attention_noalloc",
                                     "pkv_paged_attention_workspace_size", "pkv_read_stats_init",
                                     "pkv_read_stats_record", "pkv_read_stats_record_read",
                                     "pkv_read_stats_saving", "pkv_read_stats_since", "pkv_read_tile",
@@ -46,7 +47,7 @@ def test_library_exports_every_declared_symbol(lib):
 
 
 def test_status_strings(lib):
-    for code in range(0, 13):
+    for code in range(0, 14):
         assert lib.pkv_strerror(code).decode() != "unknown status"
     assert lib.pkv_strerror(0).decode() == "ok"
     assert lib.pkv_strerror(999).decode() == "unknown status"
@@ -153,6 +154,26 @@ def test_default_partitions_stated_in_the_header(lib):
     assert ws(lib, head_dim=16) == part_ws(64, 32, 4, 16)                       # bf16 hd 16: 1024
     # the stream read: header and two slots per wave, whatever the slice minimum
     assert ws(lib) == ws(lib, partition_tokens=1024) > 0
+
+
+def noalloc(lib, d, q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, cl=FAKE, out=FAKE):
+    return lib.pkv_paged_attention_noalloc(ctypes.byref(d) if d is not None else None, q, kp, vp, bt, cl,
+                                           ctypes.c_float(1.0), out, None)
+
+
+def test_noalloc_read_refusals(lib):
+    # every check of pkv_paged_attention except the workspace, then the
+    # static scratch's size; all before any HIP call
+    assert noalloc(lib, None) == 1
+    assert noalloc(lib, desc(head_dim=96)) == 5
+    assert noalloc(lib, desc(), q=0) == 1
+    assert noalloc(lib, desc(), out=FAKE + 8) == 2
+    assert noalloc(lib, desc(rows=0)) == 0  # empty: nothing to do, no scratch looked up
+    # fp32, 8192 rows x 32 heads x 64 partitions of 64 positions: 277 MB of partials
+    big = desc(rows=8192, dtype=0, out_dtype=0)
+    assert ws(lib, rows=8192, dtype=0, out_dtype=0) > 32 << 20
+    assert noalloc(lib, big) == 13
+    assert lib.pkv_strerror(13).decode().startswith("the read needs more scratch")
 
 
 def attn(lib, d, q=FAKE, kp=FAKE, vp=FAKE, bt=FAKE, cl=FAKE, out=FAKE, wsp=FAKE, wsb=1 << 40):
