@@ -69,6 +69,8 @@ def parse():
                     help="skip the other workloads (small fp32 reads, skewed batch, decode runs)")
     ap.add_argument("--prompt-scatter-only", action="store_true",
                     help="time only the 65536-token prompt scatter (for profiling)")
+    ap.add_argument("--prompt-block-size", type=int, default=16,
+                    help="pool block size of the --prompt-scatter-only workload (8, 16 or 32)")
     ap.add_argument("--prefill-chunk-only", action="store_true",
                     help="only time the multi-query read of a 64-query chunk over 16 rows of the 8B "
                          "layer (the prefill_chunk entry of other_workloads) and print it")
@@ -253,7 +255,7 @@ def other_workloads(dev, stream):
     return res
 
 
-def prompt_scatter(dev, stream, rows=128, prompt=512, calls=20):
+def prompt_scatter(dev, stream, rows=128, prompt=512, calls=20, block_size=16):
     """The slot-mapping scatter of a whole prompt batch (rows x prompt tokens,
     each row's prompt in consecutive slots of its blocks, 8 kv heads, head_dim
     128, bf16, blocks of 16): µs per call and the HBM rate of the bytes it
@@ -263,7 +265,7 @@ def prompt_scatter(dev, stream, rows=128, prompt=512, calls=20):
     import paged_kv_cache_13_amd as pkv
     from paged_kv_cache_13_amd import harness, synth
 
-    run = synth.DecodeRun(rows=rows, block_size=16, prompt=prompt, steps=0, device=dev, seed=11)
+    run = synth.DecodeRun(rows=rows, block_size=block_size, prompt=prompt, steps=0, device=dev, seed=11)
     k, v, slots = run.prefill()
 
     def call():
@@ -273,7 +275,8 @@ def prompt_scatter(dev, stream, rows=128, prompt=512, calls=20):
         call()
     mean, med = _timed(call, stream, calls, lead_cycles=1000000)
     nb = harness.scatter_bytes(k.shape[0], k.shape[1], k.shape[2], 2)
-    return {"tokens": int(k.shape[0]), "bytes": nb, "us": round(mean, 2), "us_median": round(med, 2),
+    return {"tokens": int(k.shape[0]), "block_size": block_size, "bytes": nb, "us": round(mean, 2),
+            "us_median": round(med, 2),
             "GB/s": round(nb / (mean * 1e-6) / 1e9, 1)}
 
 
@@ -409,7 +412,8 @@ def main():
     pkv.load_library()
     if args.prompt_scatter_only:
         stream = torch.cuda.current_stream()
-        print(json.dumps({"prompt_scatter": prompt_scatter(dev, stream)}), flush=True)
+        print(json.dumps({"prompt_scatter": prompt_scatter(dev, stream, block_size=args.prompt_block_size)}),
+              flush=True)
         return
     if args.prefill_chunk_only:
         stream = torch.cuda.current_stream()

@@ -181,7 +181,13 @@ struct MultiPlan {
   int32_t stream;  // 1: query_len * group <= 16 columns on the stream path
 };
 int plan_multi(const pkv_attn_desc *d, int32_t query_len, Plan *pl, MultiPlan *mp) {
-  const int st = plan_decode(d, pl);
+  if (!d) return PKV_ERR_NULL;
+  if (d->partition_tokens < 0) return PKV_ERR_PARTITION;
+  // The shapes are checked as for the one-query read, without its partition
+  // rule: this read rounds the caller's length to whole groups itself.
+  pkv_attn_desc dd = *d;
+  dd.partition_tokens = 0;
+  const int st = plan_decode(&dd, pl);
   if (st != PKV_OK) return st;
   if (d->dtype != PKV_BF16) return PKV_ERR_DTYPE;
   if (d->head_dim != 64 && d->head_dim != 128) return PKV_ERR_HEAD_DIM;
@@ -198,6 +204,9 @@ int plan_multi(const pkv_attn_desc *d, int32_t query_len, Plan *pl, MultiPlan *m
                (int64_t)d->rows * d->n_kv_heads * cap_groups >= kStreamMultiGroups * pkv::kStreamWaves;
   if (mp->stream) {
     mp->q_tiles = mp->q_per_tile = mp->q_blocks = 0;
+    if (d->partition_tokens)  // the minimum slice, in whole groups, as on the one-query read
+      pl->cg_min = (int32_t)std::min<int64_t>((d->partition_tokens + pkv::kGroupPositions - 1) / pkv::kGroupPositions,
+                                              cap_groups);
     pl->ws_bytes =
         d->rows > 0 ? pkv::stream_layout(d->rows, query_len * pl->group, d->head_dim).total * sizeof(int32_t) : 0;
     return PKV_OK;

@@ -60,3 +60,28 @@ def oracle_read(batch, rows=None):
         rows = np.arange(batch.cfg.rows)
     q, kp, vp, table, lens = host_rows(batch, rows)
     return oracle.paged_attention(q, kp, vp, table, lens, batch.scale)
+
+
+def oracle_read_parallel(batch, rows=None, threads=16):
+    """oracle_read over many rows, the unchanged oracle called on several row
+    shares at once from a thread pool (ctypes releases the GIL during the
+    call).  Shares are dealt longest row first, round-robin, so they hold
+    about the same number of positions."""
+    import concurrent.futures
+
+    if rows is None:
+        rows = np.arange(batch.cfg.rows)
+    rows = np.asarray(rows)
+    order = rows[np.argsort(-batch.ctx_host[rows], kind="stable")]
+    shares = [np.sort(order[i::threads]) for i in range(threads)]
+    shares = [sh for sh in shares if sh.size]
+    inputs = [host_rows(batch, sh) for sh in shares]
+    oracle._load()
+    with concurrent.futures.ThreadPoolExecutor(len(shares)) as ex:
+        outs = list(ex.map(lambda a: oracle.paged_attention(a[0], a[1], a[2], a[3], a[4], batch.scale), inputs))
+    ref = np.zeros((rows.size,) + outs[0].shape[1:], dtype=np.float64)
+    pos = {int(r): i for i, r in enumerate(rows)}
+    for sh, out in zip(shares, outs):
+        for j, r in enumerate(sh):
+            ref[pos[int(r)]] = out[j]
+    return ref

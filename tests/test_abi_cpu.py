@@ -341,6 +341,15 @@ def test_multi_query_refusals(lib):
     assert multi(lib, desc(), 70000) == 7
     assert multi(lib, desc(), 4, q=0) == 1
     assert multi(lib, desc(), 4, wsb=8) == 8
+    assert multi(lib, desc(partition_tokens=-32), 8) == 9
+    # the multi-query partition is rounded up to 32 positions and capped at
+    # 4096, so lengths the one-query read would refuse are taken: not a
+    # multiple of the block size, or more than 4096 blocks
+    mws = lambda d, q: lib.pkv_paged_attention_multi_workspace_size(ctypes.byref(d), q)
+    assert mws(desc(partition_tokens=40), 8) == mws(desc(partition_tokens=64), 8) > 0
+    assert mws(desc(partition_tokens=40), 4) == mws(desc(partition_tokens=64), 4) > 0  # stream path
+    big = dict(block_size=8, max_blocks_per_row=8192, num_blocks=70000)
+    assert mws(desc(partition_tokens=40000, **big), 8) == mws(desc(partition_tokens=4096, **big), 8) > 0
 
 
 def test_multi_query_workspace(lib):

@@ -15,7 +15,7 @@ import torch
 import oracle
 import paged_kv_cache_13_amd as pkv
 from paged_kv_cache_13_amd import harness, synth
-from parity import DEV, TOL, assert_close, gpu_read, oracle_read
+from parity import DEV, TOL, assert_close, gpu_read, oracle_read, oracle_read_parallel
 
 pytestmark = pytest.mark.gpu
 
@@ -140,19 +140,18 @@ def test_read_matches_oracle_full(name):
         assert_close(got32.cpu(), ref, what=name + " fp32 out", **TOL[torch.float32])
 
 
-def test_read_skewed_long_sampled_rows():
+def test_read_skewed_long_all_rows():
+    # every one of the 256 rows (1.1 M positions, lengths log-uniform in
+    # [16, 32768]) against the oracle, run on 16 row shares at once
     cfg = synth.CONFIGS["skewed_long"]
-    note("read skewed_long (sampled rows)")
+    note("read skewed_long (all rows)")
     b = synth.make_batch(cfg, device=DEV)
-    order = np.argsort(b.ctx_host)
-    rng = np.random.default_rng(0)
-    rows = np.unique(np.concatenate([order[:4], order[-6:], rng.choice(cfg.rows, 10, replace=False)]))
-    ref = oracle_read(b, rows)
-    got = gpu_read(b)[torch.as_tensor(rows, device=DEV)]
-    assert_close(got.float().cpu(), ref, what="skewed_long", **TOL[torch.bfloat16])
-    got32 = gpu_read(b, out_dtype=torch.float32)[torch.as_tensor(rows, device=DEV)]
-    assert_close(got32.cpu(), ref, what="skewed_long fp32 out", **TOL[torch.float32])
-    assert b.ctx_host[rows].max() > 16384  # the long tail is in the sample
+    got = gpu_read(b).float().cpu()
+    got32 = gpu_read(b, out_dtype=torch.float32).cpu()
+    ref = oracle_read_parallel(b)
+    assert_close(got, ref, what="skewed_long", **TOL[torch.bfloat16])
+    assert_close(got32, ref, what="skewed_long fp32 out", **TOL[torch.float32])
+    assert b.ctx_host.max() > 16384 and b.ctx_host.min() < 64  # both tails of the mix
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -594,6 +593,9 @@ def multi_oracle(b, q):
     # the 8-wave block (8-group ring) with 8-position blocks (four per
     # group) and 32-position blocks, default partitions
     (32, 8, 128, 8, 200, 900, 64, 0), (32, 8, 128, 32, 200, 900, 64, 0),
+    # partition lengths the one-query read would refuse, rounded up to
+    # whole 32-position groups: 40 at block 16 (-> 64), 100 at block 8 (-> 128)
+    (32, 8, 128, 16, 100, 400, 24, 40), (8, 1, 64, 8, 100, 500, 40, 100),
 ])
 def test_multi_query_read_matches_oracle(H, KV, hd, bs, lo, hi, qlen, part):
     note("multi H=%d KV=%d hd=%d bs=%d q=%d part=%d" % (H, KV, hd, bs, qlen, part))
@@ -607,6 +609,7 @@ def test_multi_query_read_matches_oracle(H, KV, hd, bs, lo, hi, qlen, part):
 @pytest.mark.parametrize("H,KV,hd,bs,lo,hi,qlen,part", [
     (32, 8, 128, 16, 1, 700, 4, 64), (32, 8, 128, 8, 1, 600, 4, 32), (64, 8, 64, 32, 1, 500, 2, 0),
     (16, 16, 128, 16, 1, 400, 16, 96), (16, 8, 128, 16, 30, 900, 8, 0), (32, 8, 128, 16, 1, 300, 1, 0),
+    (32, 8, 128, 16, 1, 700, 4, 40),  # a slice minimum of 40 positions: two groups
 ])
 def test_multi_query_stream_path_matches_oracle(H, KV, hd, bs, lo, hi, qlen, part):
     note("multi stream H=%d KV=%d hd=%d bs=%d q=%d part=%d" % (H, KV, hd, bs, qlen, part))
