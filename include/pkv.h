@@ -20,21 +20,10 @@
  *     must not read device values back on the host (no sync).
  *
  * Layout (all buffers device memory, row-major, contiguous, 16-byte aligned):
- *   k_pool         : [num_blocks, n_kv_heads, block_size, head_dim]
- *   v_pool         : [num_blocks, n_kv_heads, head_dim, block_size]
- *                    (each (block, kv head) tile is one contiguous run; inside
- *                    it K is position-major and V dimension-major, so both
- *                    contractions of the read find their reduction index
- *                    contiguous: head_dim for q.K, positions for p.V)
- *   The V pool departs from the position-major [num_blocks, n_kv_heads,
- *   block_size, head_dim] pool of the nanoserve-style interface (the pages
- *   name no layout; slot semantics are the same).  The trade, measured on an
- *   8B-shaped layer (64 rows, 8 kv heads, head_dim 128, bf16): the read's
- *   P.V fragments load as contiguous 16-byte runs, while appending a token
- *   writes its V row as head_dim 2-byte stores block_size elements apart --
- *   a decode step's 64 tokens (0.26 MB of K + V) cost about 2.2 MB of HBM
- *   writes and 2.9 us of a 100 us step.  A caller holding position-major V
- *   pools must transpose them once; the scatter below writes this layout.
+ *   k_pool, v_pool : [num_blocks, n_kv_heads, block_size, head_dim] each
+ *                    (position-major: a slot's K or V row for one kv head is
+ *                    head_dim contiguous elements, and each (block, kv head)
+ *                    tile is one contiguous run of block_size rows)
  *   q, out         : [rows, n_heads, head_dim]
  *   k, v (scatter) : [num_tokens, n_kv_heads, head_dim]
  *   slot_mapping   : [num_tokens] int64; slot s = block * block_size + offset
@@ -135,13 +124,13 @@ typedef struct pkv_attn_desc {
  *
  * For each token t with s = slot_mapping[t] >= 0: for every kv head g,
  * k_pool[s / block_size, g, s % block_size, :] = k[t, g, :] and
- * v_pool[s / block_size, g, :, s % block_size] = v[t, g, :], copied bit for
+ * v_pool[s / block_size, g, s % block_size, :] = v[t, g, :], copied bit for
  * bit.  Tokens with a negative slot are skipped (padding).
  *
  *   k, v          device [num_tokens, n_kv_heads, head_dim] of `dtype`
  *   slot_mapping  device [num_tokens] int64
  *   k_pool        device [num_blocks, n_kv_heads, block_size, head_dim]
- *   v_pool        device [num_blocks, n_kv_heads, head_dim, block_size]
+ *   v_pool        device [num_blocks, n_kv_heads, block_size, head_dim]
  *   num_tokens >= 0 (0 enqueues nothing); num_blocks >= 1
  * Caller contract (not checked on device): slots < num_blocks * block_size
  * (larger ones are skipped) and distinct within one call (duplicates race).
@@ -168,7 +157,7 @@ int pkv_reshape_and_cache(const void *k, const void *v, const int64_t *slot_mapp
  *   d             shapes and dtypes (host struct, read during the call only)
  *   q             device [rows, n_heads, head_dim] of d->dtype
  *   k_pool        device [num_blocks, n_kv_heads, block_size, head_dim]
- *   v_pool        device [num_blocks, n_kv_heads, head_dim, block_size]
+ *   v_pool        device [num_blocks, n_kv_heads, block_size, head_dim]
  *   block_table   device [rows, max_blocks_per_row] int32
  *   context_lens  device [rows] int32
  *   scale         softmax scale applied to the fp32 dot product

@@ -112,8 +112,8 @@ def _check(rc, what):
 
 
 def reshape_and_cache(k, v, slot_mapping, k_pool, v_pool):
-    """Scatter k, v [T, n_kv, hd] into k_pool [nb, n_kv, bs, hd] and v_pool
-    [nb, n_kv, hd, bs] in place.
+    """Scatter k, v [T, n_kv, hd] into k_pool and v_pool [nb, n_kv, bs, hd]
+    in place.
 
     Pools must be writable host arrays/tensors; they are modified in place.
     """
@@ -126,7 +126,7 @@ def reshape_and_cache(k, v, slot_mapping, k_pool, v_pool):
     sm = np.ascontiguousarray(np.asarray(slot_mapping, dtype=np.int64))
     T, n_kv, hd = kr.shape
     nb, n_kv2, bs, hd2 = kp.shape
-    if ((n_kv, hd) != (n_kv2, hd2) or vr.shape != kr.shape or vp_.shape != (nb, n_kv, hd, bs)
+    if ((n_kv, hd) != (n_kv2, hd2) or vr.shape != kr.shape or vp_.shape != (nb, n_kv, bs, hd)
             or sm.shape != (T,)):
         raise ValueError("shape mismatch")
     # the pools must be modified in place: refuse copies
@@ -147,8 +147,8 @@ def _attn_common(q, k_pool, v_pool):
         raise TypeError("q and pools must share one float dtype")
     rows, n_heads, hd = qr.shape
     nb, n_kv, bs, hd2 = kp.shape
-    if hd != hd2 or vp_.shape != (nb, n_kv, hd, bs):
-        raise ValueError("shape mismatch: k_pool [nb, n_kv, bs, hd], v_pool [nb, n_kv, hd, bs]")
+    if hd != hd2 or vp_.shape != (nb, n_kv, bs, hd):
+        raise ValueError("shape mismatch: k_pool and v_pool [nb, n_kv, bs, hd]")
     return qr, kp, vp_, dt, rows, n_heads, hd, nb, n_kv, bs
 
 

@@ -28,8 +28,8 @@
  * Layout conventions (the pages leave the pool layout open; this is the
  * reading adopted for both sides of the test):
  *   k_pool         : [num_blocks, n_kv_heads, block_size, head_dim]
- *   v_pool         : [num_blocks, n_kv_heads, head_dim, block_size]
- *                    (inside a block, V is stored dimension-major)
+ *   v_pool         : [num_blocks, n_kv_heads, block_size, head_dim]
+ *                    (the same position-major layout as K)
  *   q              : [rows, n_heads, head_dim]
  *   k, v (scatter) : [num_tokens, n_kv_heads, head_dim]
  *   slot s         : block s / block_size, offset s % block_size
@@ -70,8 +70,8 @@ static double widen(const void *base, int64_t idx, int32_t dtype) {
 /* ------------------------------------------------------------------------ */
 /* Scatter: for each new token t in ascending order, its slot s picks       */
 /* (block s / bs, offset s % bs); the token's K and V rows for every kv     */
-/* head are copied there bit for bit (V element by element into its         */
-/* dimension-major tile).  A negative slot is padding and is skipped.       */
+/* head are copied there bit for bit.  A negative slot is padding and is    */
+/* skipped.                                                                 */
 /* Duplicate slots leave the last writer (never relied upon).               */
 /* ------------------------------------------------------------------------ */
 int oracle_reshape_and_cache(const void *k, const void *v,
@@ -98,13 +98,8 @@ int oracle_reshape_and_cache(const void *k, const void *v,
     for (g = 0; g < n_kv_heads; ++g) {
       size_t src = ((size_t)t * n_kv_heads + g) * row_bytes;
       size_t dst = (((size_t)blk * n_kv_heads + g) * block_size + off) * row_bytes;
-      int32_t d;
       memcpy((unsigned char *)k_pool + dst, (const unsigned char *)k + src, row_bytes);
-      /* V: element d of the row goes to [blk][g][d][off] */
-      for (d = 0; d < head_dim; ++d) {
-        size_t vdst = ((((size_t)blk * n_kv_heads + g) * head_dim + d) * block_size + off) * es;
-        memcpy((unsigned char *)v_pool + vdst, (const unsigned char *)v + src + (size_t)d * es, es);
-      }
+      memcpy((unsigned char *)v_pool + dst, (const unsigned char *)v + src, row_bytes);
     }
   }
   return ORC_OK;
@@ -195,12 +190,10 @@ static int gathered_read(int32_t rows, int32_t n_heads, int32_t n_kv_heads,
       blk = sl / block_size;
       off = sl % block_size;
       for (g = 0; g < n_kv_heads; ++g) {
-        int64_t ksrc = (((int64_t)blk * n_kv_heads + g) * block_size + off) * head_dim;
-        int64_t vtile = ((int64_t)blk * n_kv_heads + g) * head_dim;
+        int64_t src = (((int64_t)blk * n_kv_heads + g) * block_size + off) * head_dim;
         for (d = 0; d < head_dim; ++d) {
-          Kc[((size_t)t * n_kv_heads + g) * head_dim + d] = widen(k_pool, ksrc + d, dtype);
-          Vc[((size_t)t * n_kv_heads + g) * head_dim + d] =
-              widen(v_pool, (vtile + d) * block_size + off, dtype);
+          Kc[((size_t)t * n_kv_heads + g) * head_dim + d] = widen(k_pool, src + d, dtype);
+          Vc[((size_t)t * n_kv_heads + g) * head_dim + d] = widen(v_pool, src + d, dtype);
         }
       }
     }
@@ -360,11 +353,10 @@ int oracle_paged_attention_streamed(int32_t rows, int32_t n_heads,
         for (t = 0; t < w; ++t) {
           int64_t pos = start + t;
           int64_t blk = block_table[(size_t)r * max_blocks_per_row + pos / block_size];
-          int64_t vtile = (blk * n_kv_heads + kvh) * head_dim;
+          int64_t vrow = ((blk * n_kv_heads + kvh) * block_size + pos % block_size) * head_dim;
           double p = exp(st[t] - m_new);
           l += p;
-          for (d = 0; d < head_dim; ++d)
-            acc[d] += p * widen(v_pool, (vtile + d) * block_size + pos % block_size, dtype);
+          for (d = 0; d < head_dim; ++d) acc[d] += p * widen(v_pool, vrow + d, dtype);
         }
         m = m_new;
       }
@@ -431,12 +423,10 @@ int oracle_paged_attention_multi(int32_t rows, int32_t query_len, int32_t n_head
         return ORC_ERANGE;
       }
       for (g = 0; g < n_kv_heads; ++g) {
-        int64_t ksrc = (((int64_t)blk * n_kv_heads + g) * block_size + off) * head_dim;
-        int64_t vtile = ((int64_t)blk * n_kv_heads + g) * head_dim;
+        int64_t src = (((int64_t)blk * n_kv_heads + g) * block_size + off) * head_dim;
         for (d = 0; d < head_dim; ++d) {
-          Kc[((size_t)t * n_kv_heads + g) * head_dim + d] = widen(k_pool, ksrc + d, dtype);
-          Vc[((size_t)t * n_kv_heads + g) * head_dim + d] =
-              widen(v_pool, (vtile + d) * block_size + off, dtype);
+          Kc[((size_t)t * n_kv_heads + g) * head_dim + d] = widen(k_pool, src + d, dtype);
+          Vc[((size_t)t * n_kv_heads + g) * head_dim + d] = widen(v_pool, src + d, dtype);
         }
       }
     }

@@ -143,8 +143,8 @@ def _on_gpu(*ts):
 def _check_pools(k_pool, v_pool):
     _require(k_pool.dim() == 4, "k_pool must be [num_blocks, n_kv_heads, block_size, head_dim]")
     nb, nkv, bs, hd = k_pool.shape
-    _require(tuple(v_pool.shape) == (nb, nkv, hd, bs),
-             "v_pool must be [num_blocks, n_kv_heads, head_dim, block_size]")
+    _require(tuple(v_pool.shape) == (nb, nkv, bs, hd),
+             "v_pool must be [num_blocks, n_kv_heads, block_size, head_dim]")
 
 
 def _stream_handle(device) -> int:
@@ -153,9 +153,8 @@ def _stream_handle(device) -> int:
 
 def reshape_and_cache(k: torch.Tensor, v: torch.Tensor, slot_mapping: torch.Tensor,
                       k_pool: torch.Tensor, v_pool: torch.Tensor) -> None:
-    """Scatter k, v [T, n_kv, hd] into k_pool [nb, n_kv, bs, hd] and v_pool
-    [nb, n_kv, hd, bs] at slot_mapping [T] (int64; negative = skip), on the
-    current stream."""
+    """Scatter k, v [T, n_kv, hd] into k_pool and v_pool [nb, n_kv, bs, hd]
+    at slot_mapping [T] (int64; negative = skip), on the current stream."""
     dev = _on_gpu(k, v, slot_mapping, k_pool, v_pool)
     _require(k.dim() == 3 and v.shape == k.shape, "k, v must be [T, n_kv_heads, head_dim]")
     _check_pools(k_pool, v_pool)

@@ -156,25 +156,6 @@ __device__ __forceinline__ uint4 load16(const void *base, size_t byte_off) {
   return *reinterpret_cast<const uint4 *>(static_cast<const char *>(base) + byte_off);
 }
 
-// 16 bytes of one position's V row from a dimension-major tile: consecutive
-// elements are `stride` elements apart starting at element index `first`.
-template <typename T>
-__device__ __forceinline__ uint4 gather_v(const void *base, size_t first, int stride);
-template <>
-__device__ __forceinline__ uint4 gather_v<float>(const void *base, size_t first, int stride) {
-  const uint32_t *p = static_cast<const uint32_t *>(base) + first;
-  return make_uint4(p[0], p[stride], p[2 * stride], p[3 * stride]);
-}
-template <>
-__device__ __forceinline__ uint4 gather_v<uint16_t>(const void *base, size_t first, int stride) {
-  const uint16_t *p = static_cast<const uint16_t *>(base) + first;
-  uint32_t w[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-    w[i] = (uint32_t)p[(2 * i) * stride] | ((uint32_t)p[(2 * i + 1) * stride] << 16);
-  return make_uint4(w[0], w[1], w[2], w[3]);
-}
-
 // Work item of this workgroup.  The grid is 1-D and ordered kv head fastest,
 // then row, then partition.  Workgroups are handed to the 8 XCDs round-robin
 // by linear id, so this order gives every XCD the same mix of full, partial
@@ -208,10 +189,10 @@ __device__ __forceinline__ void append_store_row(const DecodeArgs &a, int r, int
   E *kp = static_cast<E *>(const_cast<void *>(a.k_pool)) +
           ((((size_t)blk * a.n_kv_heads + kvh) << a.log2_bs) + off) * a.head_dim;
   E *vp = static_cast<E *>(const_cast<void *>(a.v_pool)) +
-          ((((size_t)blk * a.n_kv_heads + kvh) * a.head_dim) << a.log2_bs) + off;
+          ((((size_t)blk * a.n_kv_heads + kvh) << a.log2_bs) + off) * a.head_dim;
   for (int d = t0; d < a.head_dim; d += nthreads) {
     kp[d] = kn[d];
-    vp[(size_t)d << a.log2_bs] = vn[d];
+    vp[d] = vn[d];
   }
 }
 
@@ -318,9 +299,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition(DecodeArgs a) {
         const size_t tile = (size_t)blk * tile_stride + g;
         const size_t row = (tile << a.log2_bs) + (t & bmask);
         kr[i] = load16(a.k_pool, (row * HD + c * EPL) * ES);
-        // V tile is dimension-major: element d of position o at [d][o]
-        vr[i] = gather_v<T>(a.v_pool, ((tile * HD + c * EPL) << a.log2_bs) + (t & bmask),
-                            a.block_size);
+        vr[i] = load16(a.v_pool, (row * HD + c * EPL) * ES);
       }
     }
     // scores
@@ -451,7 +430,8 @@ __global__ __launch_bounds__(128) void decode_merge(DecodeArgs a) {
 //                      A = K rows (position-major tile), B = Q, two 16-row
 //                      tiles per 32 positions, head_dim / 32 k-steps each;
 //   output  O[d][h] += sum_t V[d][t] P[h][t]      same instruction, A = V
-//                      (dimension-major tile), B = P, head_dim / 16 d-tiles.
+//                      (read transposed out of a position-major LDS tile,
+//                      see v_tile_frag), B = P, head_dim / 16 d-tiles.
 // Row m of score tile tt is position 8*(m/4) + 4*tt + m%4 of the 32, so the
 // 4 accumulator rows a lane receives from the two tiles are 8 consecutive
 // positions 8*(lane/16) .. +7 for head lane%16 -- exactly the 8 k-values that
@@ -504,10 +484,63 @@ __device__ __forceinline__ bf16x8_t keep_first(bf16x8_t v, int nv) {
   return __builtin_bit_cast(bf16x8_t, make_uint4(x[0], x[1], x[2], x[3]));
 }
 
+// V comes out of the pool position-major, as K does: a 32-position group is
+// 32 rows of head_dim bf16.  The P.V product needs, per lane, 8 consecutive
+// positions of one dimension, so the group is staged in LDS as rows and read
+// back with ds_read_b64_tr_b16: within each 16 lanes, lanes 4r .. 4r + 3
+// name the four 8-byte pieces of row r of a 4 x 16 block (lane 4r + q:
+// columns 4q .. 4q + 3) and lane i receives column i of rows 0 .. 3.
+//
+// Staged tile: row p (group position) at p * 2 head_dim bytes, its logical
+// 16-byte chunk c at physical chunk c ^ vswz16(p).  The XOR keeps every
+// transposed read free of bank conflicts (each 16-, 32- or 64-lane set of a
+// read touches distinct banks) and leaves bit 2 of p alone, so the second
+// read of a fragment (rows p + 4) is the first one's address plus 4 rows.
+template <int HD>
+__device__ __forceinline__ int vswz16(int p) {
+  const int b0 = p & 1, b1 = (p >> 1) & 1, b3 = (p >> 3) & 1, b4 = (p >> 4) & 1;
+  return HD == 128 ? 2 * ((b0 ^ b4) | (b1 << 1) | (b3 << 2)) : 2 * ((b0 ^ b3) | ((b1 ^ b4) << 1));
+}
+
+typedef short v4i16_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ uint2 lds_read_tr16(const void *lds, uint32_t byte_off) {
+  auto *p = (__attribute__((address_space(3))) v4i16_t *)((__attribute__((address_space(3))) char *)lds + byte_off);
+  return __builtin_bit_cast(uint2, __builtin_amdgcn_ds_read_tr16_b64_v4i16(p));
+}
+
+// Byte offset, in a staged V tile, of this lane's first transposed read of
+// d-tile 0 (rows 8 lg + lr / 4, dims 4 (lr % 4) .. + 3); d-tile dt is that
+// offset XOR 32 dt, the second read 4 rows further.
+template <int HD>
+__device__ __forceinline__ uint32_t v_tile_lane(int lr, int lg) {
+  const int p = 8 * lg + (lr >> 2), q = lr & 3;
+  return (uint32_t)(p * 2 * HD + 16 * ((q >> 1) ^ vswz16<HD>(p)) + 8 * (q & 1));
+}
+
+// V fragment dt of lane (lr, lg): dim 16 dt + lr at positions 8 lg .. + 7.
+template <int HD>
+__device__ __forceinline__ bf16x8_t v_tile_frag(const void *tile, uint32_t lane_off, int dt) {
+  const uint32_t o = lane_off ^ (uint32_t)(32 * dt);
+  const uint2 lo = lds_read_tr16(tile, o), hi = lds_read_tr16(tile, o + 8 * HD);
+  return __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+}
+
+// Source of the 16 bytes that load i of a tile fill (LDS chunk 64 i + lane):
+// group row p, logical chunk c.  A load covers 64 / (head_dim / 8) whole
+// consecutive rows, which lie in one pool block.
+template <int HD>
+__device__ __forceinline__ void v_tile_src(int i, int lane, int &p, int &c) {
+  constexpr int CPR = HD / 8, PPL = kWave / CPR;
+  p = PPL * i + lane / CPR;
+  c = (lane % CPR) ^ vswz16<HD>(p);
+}
+
+// s_waitcnt immediate for vmcnt(n) and lgkmcnt(0) (expcnt left alone).
+__host__ __device__ constexpr int vmcnt_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
+
 template <int HD>
 struct MfmaTiles {
   bf16x8_t k[2][HD / 32];  // score tiles x k-steps
-  bf16x8_t v[HD / 16];     // output d-tiles
 };
 
 // Issue the loads of one 32-position group.  Branch-free: positions at or
@@ -515,7 +548,7 @@ struct MfmaTiles {
 // mapped), and are masked where they are used, so the loads of the next group
 // can be in flight while this one is computed.
 template <int HD, int BS>
-__device__ __forceinline__ void mfma_load(MfmaTiles<HD> &T, const DecodeArgs &a, const int32_t *s_blk,
+__device__ __forceinline__ void mfma_load(MfmaTiles<HD> &T, uint4 *vtile, const DecodeArgs &a, const int32_t *s_blk,
                                           int g, int start, int end, int gbase, int lr, int lg) {
   constexpr int KS = HD / 32, DT = HD / 16;
   constexpr int LOG2_BS = BS == 8 ? 3 : (BS == 16 ? 4 : 5);
@@ -530,19 +563,46 @@ __device__ __forceinline__ void mfma_load(MfmaTiles<HD> &T, const DecodeArgs &a,
 #pragma unroll
     for (int i = 0; i < KS; ++i) T.k[tt][i] = ld_bf16x8(kp, i * 64);
   }
-  int t0 = gbase + 8 * lg;
-  t0 = t0 < end ? t0 : start;
-  const int32_t blk = s_blk[(t0 - start) >> LOG2_BS];
-  const size_t base = ((((size_t)blk * a.n_kv_heads + g) * HD + lr) << LOG2_BS) + (t0 & bmask);
-  const char *vp = static_cast<const char *>(a.v_pool) + base * 2;
+  // V rows straight into the wave's LDS tile `vtile` (direct-to-LDS loads,
+  // no registers).  Rows past `end` read row end - 1 instead.  A load's rows
+  // are one aligned run of 64 / (head_dim / 8) positions, so they (clamped
+  // or not) share the block of the run's first position, clamped the same way.
+  constexpr int PPL = kWave / (HD / 8);
+  const int lane = 16 * lg + lr;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt) T.v[dt] = ld_bf16x8(vp, dt * 16 * BS * 2);
+  for (int i = 0; i < DT; ++i) {
+    int p, col;
+    v_tile_src<HD>(i, lane, p, col);
+    const int t = min(gbase + p, end - 1);
+    const int32_t blk =
+        __builtin_amdgcn_readfirstlane(s_blk[(min(gbase + PPL * i, end - 1) - start) >> LOG2_BS]);
+    const char *vb = static_cast<const char *>(a.v_pool) + ((((size_t)blk * a.n_kv_heads + g) << LOG2_BS) * HD) * 2 +
+                     (uint32_t)(((t & bmask) * HD + 8 * col) * 2);
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)vb,
+                                     (void __attribute__((address_space(3))) *)(vtile + i * kWave), 16, 0, 0);
+  }
+}
+
+// Until only the next group's loads (issued after this group's) are in
+// flight: this group's K registers and V tile have landed.  The compiler
+// orders neither the V tile's LDS reads after its direct-to-LDS loads nor
+// (by itself) the K registers' wait before them, so the wait is explicit.
+template <int HD>
+__device__ __forceinline__ void mfma_wait_group(bool next_in_flight) {
+  constexpr int kNextLoads = 2 * (HD / 32) + HD / 16;  // K then V loads of one group
+  asm volatile("" ::: "memory");
+  if (next_in_flight)
+    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(kNextLoads));
+  else
+    __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
+  asm volatile("" ::: "memory");
 }
 
 // Online-softmax step over one loaded group (see the block comment above).
 template <int HD>
 __device__ __forceinline__ void mfma_compute(MfmaTiles<HD> &T, const bf16x8_t *qb, f32x4_t *acc, float &m,
-                                             float &l, float c, int end, int gbase, int lg) {
+                                             float &l, float c, int end, int gbase, int lg, const uint4 *s_vw,
+                                             uint32_t v_lane) {
   constexpr int KS = HD / 32, DT = HD / 16;
   f32x4_t sacc[2] = {f32x4_t{0.f, 0.f, 0.f, 0.f}, f32x4_t{0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
@@ -585,6 +645,9 @@ __device__ __forceinline__ void mfma_compute(MfmaTiles<HD> &T, const bf16x8_t *q
   }
   const bf16x8_t phi = __builtin_bit_cast(bf16x8_t, make_uint4(hw[0], hw[1], hw[2], hw[3]));
   const bf16x8_t plo = __builtin_bit_cast(bf16x8_t, make_uint4(lw[0], lw[1], lw[2], lw[3]));
+  bf16x8_t vf[DT];
+#pragma unroll
+  for (int dt = 0; dt < DT; ++dt) vf[dt] = v_tile_frag<HD>(s_vw, v_lane, dt);
   // The last group of a partition may hold positions past `end` (stale or
   // NaN pool slots): their weights are 0, but 0 * NaN is NaN, so the V values
   // themselves are zeroed.  Wave-uniform branch, taken once per partition.
@@ -592,12 +655,12 @@ __device__ __forceinline__ void mfma_compute(MfmaTiles<HD> &T, const bf16x8_t *q
     int nv = end - tl;
     nv = nv < 0 ? 0 : (nv > 8 ? 8 : nv);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) T.v[dt] = keep_first(T.v[dt], nv);
+    for (int dt = 0; dt < DT; ++dt) vf[dt] = keep_first(vf[dt], nv);
   }
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) {
-    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(T.v[dt], phi, acc[dt], 0, 0, 0);
-    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(T.v[dt], plo, acc[dt], 0, 0, 0);
+    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], phi, acc[dt], 0, 0, 0);
+    acc[dt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(vf[dt], plo, acc[dt], 0, 0, 0);
   }
 }
 
@@ -610,17 +673,16 @@ __device__ __forceinline__ void mfma_compute(MfmaTiles<HD> &T, const bf16x8_t *q
 // sees exactly what a scatter followed by a read would.  Slots that are
 // negative or past the pool are skipped, as the scatter skips them.
 //
-// Lane layout of a loaded group (the same for the stream kernel's LDS tile
-// and the partition kernel's registers): K tile tt, row 8 (lr / 4) + 4 tt +
-// lr % 4, dims 32 i + 8 lg .. + 8 in K fragment (tt, i) of lane (lr, lg);
-// V fragment dt of lane (lr, lg): dim 16 dt + lr at positions 8 lg .. + 7.
+// Lane layout of a loaded group in the stream kernel's LDS: K tile tt, row
+// 8 (lr / 4) + 4 tt + lr % 4, dims 32 i + 8 lg .. + 8 in K fragment (tt, i)
+// of lane (lr, lg); V as a staged tile of rows (v_tile_frag).
 template <int HD>
 struct Append {
   bool pending;        // wave-uniform: the token's group is computed next
   int p;               // the token's position in its group
   int64_t slot;        // loaded by every lane, read after the wait
   bf16x8_t k[HD / 32]; // lanes lr == append_k_lane(p): K dims 32 i + 8 lg .. + 8
-  uint16_t v[HD / 16]; // lanes lg == p / 8: V dims 16 dt + lr
+  uint4 v;             // lanes below head_dim / 8: V chunk `lane` of the row
 };
 
 __device__ __forceinline__ int append_k_lane(int p) { return ((p >> 3) << 2) | (p & 3); }
@@ -628,7 +690,7 @@ __device__ __forceinline__ int append_k_lane(int p) { return ((p >> 3) << 2) | (
 template <int HD>
 __device__ __forceinline__ void append_fetch(Append<HD> &A, const DecodeArgs &a, int r, int kvh, int p, int lr,
                                              int lg) {
-  constexpr int KS = HD / 32, DT = HD / 16;
+  constexpr int KS = HD / 32;
   A.p = p;
   A.slot = a.slot_new[r];
   const size_t base = ((size_t)r * a.n_kv_heads + kvh) * HD;
@@ -636,11 +698,8 @@ __device__ __forceinline__ void append_fetch(Append<HD> &A, const DecodeArgs &a,
 #pragma unroll
     for (int i = 0; i < KS; ++i) A.k[i] = ld_bf16x8(a.k_new, (base + i * 32 + lg * 8) * 2);
   }
-  if (lg == (p >> 3)) {
-    const uint16_t *vn = static_cast<const uint16_t *>(a.v_new) + base + lr;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) A.v[dt] = vn[dt * 16];
-  }
+  const int lane = 16 * lg + lr;
+  if (lane < HD / 8) A.v = load16(a.v_new, (base + 8 * lane) * 2);
 }
 
 // The slot, once the fetch has landed; -1 when the token is skipped.
@@ -654,7 +713,7 @@ __device__ __forceinline__ int64_t append_slot(int64_t slot, const DecodeArgs &a
 template <int HD, int BS>
 __device__ __forceinline__ void append_store_pool(const Append<HD> &A, const DecodeArgs &a, int kvh, int64_t s, int lr,
                                                   int lg) {
-  constexpr int KS = HD / 32, DT = HD / 16;
+  constexpr int KS = HD / 32;
   constexpr int LOG2_BS = BS == 8 ? 3 : (BS == 16 ? 4 : 5);
   const int64_t blk = s >> LOG2_BS;
   const int off = (int)(s & (BS - 1));
@@ -664,11 +723,11 @@ __device__ __forceinline__ void append_store_pool(const Append<HD> &A, const Dec
 #pragma unroll
     for (int i = 0; i < KS; ++i) *reinterpret_cast<uint4 *>(kp + i * 32) = __builtin_bit_cast(uint4, A.k[i]);
   }
-  if (lg == (A.p >> 3)) {
+  const int lane = 16 * lg + lr;
+  if (lane < HD / 8) {
     uint16_t *vp = static_cast<uint16_t *>(const_cast<void *>(a.v_pool)) +
-                   ((((size_t)blk * a.n_kv_heads + kvh) * HD + lr) << LOG2_BS) + off;
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) vp[(size_t)dt * 16 * BS] = A.v[dt];
+                   ((((size_t)blk * a.n_kv_heads + kvh) << LOG2_BS) + off) * HD + 8 * lane;
+    *reinterpret_cast<uint4 *>(vp) = A.v;
   }
 }
 
@@ -707,13 +766,13 @@ __device__ __forceinline__ void token_store(const TokenRow<HD> &t, const DecodeA
   uint16_t *kp = static_cast<uint16_t *>(const_cast<void *>(a.k_pool)) +
                  ((((size_t)blk * a.n_kv_heads + kvh) << LOG2_BS) + off) * HD;
   uint16_t *vp = static_cast<uint16_t *>(const_cast<void *>(a.v_pool)) +
-                 ((((size_t)blk * a.n_kv_heads + kvh) * HD) << LOG2_BS) + off;
+                 ((((size_t)blk * a.n_kv_heads + kvh) << LOG2_BS) + off) * HD;
 #pragma unroll
   for (int i = 0; i < PER; ++i) {
     const int d = lane + i * kWave;
     if (d < HD) {
       kp[d] = t.k[i];
-      vp[(size_t)d << LOG2_BS] = t.v[i];
+      vp[d] = t.v[i];
     }
   }
 }
@@ -723,7 +782,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   constexpr int KS = HD / 32, DT = HD / 16, GT = 32;
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
+  // Wave w's two V tiles (32 rows of head_dim bf16 each): s_acc[w], which
+  // holds 64 * head_dim bytes too, until the wave's last group has been
+  // read, and s_vt[w].
   __shared__ float s_acc[kWaves][16][HD];
+  __shared__ uint4 s_vt[kWaves][HD / 16 * kWave];
+  static_assert(sizeof(s_acc[0]) == sizeof(s_vt[0]), "a wave's V tile fills its s_acc row");
   extern __shared__ int32_t s_blk[];
 
   const WorkItem it = work_item(a);
@@ -783,27 +847,36 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 #pragma unroll
   for (int dt = 0; dt < DT; ++dt) acc[dt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  // Two tile sets, alternating: while one group is computed the next one's
-  // loads are in flight.  Uniform control flow only.
+  // Two tile sets (K registers, V LDS tile), alternating: while one group is
+  // computed the next one's loads are in flight.  A set's V tile is refilled
+  // only after its previous group's reads of it have returned (their values
+  // fed that group's products).  Uniform control flow only.
   constexpr int kStep = kWaves * GT;
+  uint4 *va = reinterpret_cast<uint4 *>(&s_acc[wave][0][0]);
+  uint4 *vb = s_vt[wave];
+  const uint32_t v_lane = v_tile_lane<HD>(lr, lg);
   MfmaTiles<HD> A, B;
   int gb = start + wave * GT;
   if (gb < end) {
-    mfma_load<HD, BS>(A, a, s_blk, g, start, end, gb, lr, lg);
+    mfma_load<HD, BS>(A, va, a, s_blk, g, start, end, gb, lr, lg);
     while (true) {
       if (gb + kStep >= end) {
-        mfma_compute<HD>(A, qb, acc, m, l, c, end, gb, lg);
+        mfma_wait_group<HD>(false);
+        mfma_compute<HD>(A, qb, acc, m, l, c, end, gb, lg, va, v_lane);
         break;
       }
-      mfma_load<HD, BS>(B, a, s_blk, g, start, end, gb + kStep, lr, lg);
-      mfma_compute<HD>(A, qb, acc, m, l, c, end, gb, lg);
+      mfma_load<HD, BS>(B, vb, a, s_blk, g, start, end, gb + kStep, lr, lg);
+      mfma_wait_group<HD>(true);
+      mfma_compute<HD>(A, qb, acc, m, l, c, end, gb, lg, va, v_lane);
       gb += kStep;
       if (gb + kStep >= end) {
-        mfma_compute<HD>(B, qb, acc, m, l, c, end, gb, lg);
+        mfma_wait_group<HD>(false);
+        mfma_compute<HD>(B, qb, acc, m, l, c, end, gb, lg, vb, v_lane);
         break;
       }
-      mfma_load<HD, BS>(A, a, s_blk, g, start, end, gb + kStep, lr, lg);
-      mfma_compute<HD>(B, qb, acc, m, l, c, end, gb, lg);
+      mfma_load<HD, BS>(A, va, a, s_blk, g, start, end, gb + kStep, lr, lg);
+      mfma_wait_group<HD>(true);
+      mfma_compute<HD>(B, qb, acc, m, l, c, end, gb, lg, vb, v_lane);
       gb += kStep;
     }
   }
@@ -1064,7 +1137,8 @@ __device__ __forceinline__ void plan_locate(const RowWindow &win, int rem, int l
 }
 
 struct GroupIds {
-  int32_t k0, k1, v;  // this lane's block ids: score tiles 0/1 rows, V chunk
+  int32_t k0, k1;  // this lane's block ids: its rows of score tiles 0 and 1
+  int32_t v;       // block of positions 8 lg .. of the group (V staging)
 };
 
 template <int BS>
@@ -1353,15 +1427,23 @@ __device__ __forceinline__ void stage_group(uint4 *s_k, uint4 *s_v, const Decode
                                        (void __attribute__((address_space(3))) *)(s_k + (tt * KS + i) * kWave),
                                        16, 0, kStreamingLoad);
   }
-  const int tv = min(t0 + 8 * lg, last) & ~7;
-  int64_t blk = ids.v;
-  blk = blk < 0 ? 0 : (blk > nb1 ? nb1 : blk);
-  const size_t base = ((((size_t)blk * a.n_kv_heads + c.kvh) * HD + lr) << LOG2_BS) + (tv & bmask);
-  const char *vp = static_cast<const char *>(a.v_pool) + base * 2;
+  // V: load i fills LDS chunks 64 i .. of the row tile (v_tile_src); its rows
+  // lie in the block of positions t0 + 8 q .., q = its first row / 8, whose id
+  // lane 16 q holds.  Rows past `last` read row `last` (same block).
+  constexpr int PPL = kWave / (HD / 8);
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
-    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)(vp + dt * 16 * BS * 2),
-                                     (void __attribute__((address_space(3))) *)(s_v + dt * kWave), 16, 0, kStreamingLoad);
+  for (int i = 0; i < DT; ++i) {
+    int p, col;
+    v_tile_src<HD>(i, lane, p, col);
+    int64_t blk = __builtin_amdgcn_readlane(ids.v, 16 * ((PPL * i) >> 3));
+    blk = blk < 0 ? 0 : (blk > nb1 ? nb1 : blk);
+    const int t = min(t0 + p, last);
+    const char *vp = static_cast<const char *>(a.v_pool) +
+                     ((((size_t)blk * a.n_kv_heads + c.kvh) << LOG2_BS) * HD) * 2 +
+                     (uint32_t)(((t & bmask) * HD + 8 * col) * 2);
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)vp,
+                                     (void __attribute__((address_space(3))) *)(s_v + i * kWave), 16, 0, kStreamingLoad);
+  }
 }
 
 // Stream kernel: fetch for cursor c when it is its row's last group.
@@ -1375,7 +1457,7 @@ __device__ __forceinline__ void append_load(Append<HD> &A, const DecodeArgs &a, 
 template <int HD, int BS>
 __device__ __forceinline__ void append_apply(const Append<HD> &A, const DecodeArgs &a, const Cursor &c, uint4 *s_k,
                                              uint4 *s_v, int lane, int lr, int lg) {
-  constexpr int KS = HD / 32, DT = HD / 16;
+  constexpr int KS = HD / 32;
   const int64_t s = append_slot<BS>(A.slot, a);
   if (s < 0) return;
   append_store_pool<HD, BS>(A, a, c.kvh, s, lr, lg);
@@ -1385,10 +1467,7 @@ __device__ __forceinline__ void append_apply(const Append<HD> &A, const DecodeAr
 #pragma unroll
     for (int i = 0; i < KS; ++i) s_k[(tt * KS + i) * kWave + lane] = __builtin_bit_cast(uint4, A.k[i]);
   }
-  if (lg == (p >> 3)) {
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt) reinterpret_cast<uint16_t *>(s_v + dt * kWave + lane)[p & 7] = A.v[dt];
-  }
+  if (lane < HD / 8) s_v[p * (HD / 8) + (lane ^ vswz16<HD>(p))] = A.v;
 }
 
 template <int HD, int BS>
@@ -1474,6 +1553,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
   append_load<HD>(ap, a, c0, lr, lg);
 
   bf16x8_t kc[2][KS], vc[DT];
+  const uint32_t v_lane = v_tile_lane<HD>(lr, lg);
   while (true) {
     // The staged group (and the next group's block ids) must have landed.
     // The compiler does not order LDS reads after direct-to-LDS loads by
@@ -1481,12 +1561,13 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
     __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0)
     asm volatile("" ::: "memory");
     if (ap.pending) append_apply<HD, BS>(ap, a, c0, s_k, s_v, lane, lr, lg);
+    asm volatile("" ::: "memory");
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt)
 #pragma unroll
       for (int i = 0; i < KS; ++i) kc[tt][i] = __builtin_bit_cast(bf16x8_t, s_k[(tt * KS + i) * kWave + lane]);
 #pragma unroll
-    for (int dt = 0; dt < DT; ++dt) vc[dt] = __builtin_bit_cast(bf16x8_t, s_v[dt * kWave + lane]);
+    for (int dt = 0; dt < DT; ++dt) vc[dt] = v_tile_frag<HD>(s_v, v_lane, dt);
     __builtin_amdgcn_s_waitcnt(0xC07F);  // lgkmcnt(0): the buffer may be refilled
     asm volatile("" ::: "memory");
     const bool last_group = c0.idx + 1 >= total;
@@ -1604,6 +1685,17 @@ __device__ __forceinline__ int kswz(int p) {
   return HD == 128 ? (p & 15) : ((p >> 1) & 7);
 }
 
+// V of a staged group is kept the same way, rows of positions in 1 KB slots
+// after the K slots, with its own XOR vswz32(p): the P.V operand of lane
+// (lr, h) is hd 32 dt + lr at positions 16 kk + 8 h .. + 8, read transposed
+// (lds_read_tr16) from rows p and p + 4; the XOR spreads every such read
+// over distinct banks and leaves bit 2 of p alone.
+template <int HD>
+__device__ __forceinline__ int vswz32(int p) {
+  const int b0 = p & 1, b1 = (p >> 1) & 1, b3 = (p >> 3) & 1, b4 = (p >> 4) & 1;
+  return HD == 128 ? (4 * (b0 ^ b3) | 10 * b1) : ((4 * b0) ^ (6 * b1) ^ (4 * b3) ^ (2 * b4));
+}
+
 // LDS uint4 index, within a staged group, of this lane's K fragment for
 // k-step ks: position sigma(lane % 32), hd 16 ks + 8 (lane / 32) .. + 8.
 template <int HD>
@@ -1646,50 +1738,35 @@ __device__ __forceinline__ size_t group_block(int j, int32_t id0, int32_t id1, i
   return (size_t)b;
 }
 
-// Stage one group: this wave's share of the NSLOT 1 KB slots.  K slots are
-// contiguous runs of the K tile (see kswz); V slot (dt, kk): lane l loads hd
-// row 32 dt + l % 32, positions 16 kk + 8 (l / 32) .. + 8 (one 16-byte run of
-// the dimension-major V tile).  Positions past `last` read position `last`.
+// Stage one group: this wave's share of the NSLOT 1 KB slots.  K and V slots
+// are contiguous runs of rows of the K and V tiles (see kswz, vswz32).
+// Positions past `last` read position `last`.
 template <int HD, int BS, int NW>
 __device__ __forceinline__ void stage_multi(uint4 *st, const DecodeArgs &a, const int32_t *s_blk, int blk0, int nblk,
                                             int kvh, int t0, int last, int wave, int lane) {
   constexpr int KS = HD / 16, NSLOT = HD / 8, SPW = NSLOT / NW, CPR = HD / 8, RPS = 64 / CPR;
   constexpr int LOG2_BS = BS == 8 ? 3 : (BS == 16 ? 4 : 5);
   constexpr int bmask = BS - 1;
-  const int lr = lane & 31, h = lane >> 5;
   // the group's (up to four) block ids, the same for every lane
   const int gb = (t0 >> LOG2_BS) - blk0;
   int32_t id0, id1, id2, id3;
   lds_read4(s_blk, gb, min(gb + 1, nblk - 1), min(gb + 2, nblk - 1), min(gb + 3, nblk - 1), id0, id1, id2, id3);
   const int tb0 = t0 >> LOG2_BS;
-  const int tv0 = min(t0 + 8 * h, last) & ~7, tv1 = min(t0 + 16 + 8 * h, last) & ~7;
-  const size_t bv0 = group_block<BS>((tv0 >> LOG2_BS) - tb0, id0, id1, id2, id3);
-  const size_t bv1 = group_block<BS>((tv1 >> LOG2_BS) - tb0, id0, id1, id2, id3);
-  const char *vp0 = static_cast<const char *>(a.v_pool) +
-                    ((((bv0 * a.n_kv_heads + kvh) * HD + lr) << LOG2_BS) + (tv0 & bmask)) * 2;
-  const char *vp1 = static_cast<const char *>(a.v_pool) +
-                    ((((bv1 * a.n_kv_heads + kvh) * HD + lr) << LOG2_BS) + (tv1 & bmask)) * 2;
 #pragma unroll
   for (int x = 0; x < SPW; ++x) {
     const int s = wave + NW * x;  // wave-uniform slot
-    const char *src;
-    if (s < KS) {
-      const int p = RPS * s + lane / CPR, t = min(t0 + p, last);
-      const int col = (lane % CPR) ^ kswz<HD>(p);
-      const size_t bk = group_block<BS>((t >> LOG2_BS) - tb0, id0, id1, id2, id3);
-      src = static_cast<const char *>(a.k_pool) + ((((bk * a.n_kv_heads + kvh) << LOG2_BS) + (t & bmask)) * HD + 8 * col) * 2;
-    } else {
-      const int v = s - KS;  // hd tile v / 2, position run v % 2
-      src = ((v & 1) ? vp1 : vp0) + (size_t)(v >> 1) * (32 * BS * 2);
-    }
+    const bool is_k = s < KS;
+    const int p = RPS * (is_k ? s : s - KS) + lane / CPR, t = min(t0 + p, last);
+    const int col = (lane % CPR) ^ (is_k ? kswz<HD>(p) : vswz32<HD>(p));
+    const size_t bk = group_block<BS>((t >> LOG2_BS) - tb0, id0, id1, id2, id3);
+    const char *src = static_cast<const char *>(is_k ? a.k_pool : a.v_pool) +
+                      ((((bk * a.n_kv_heads + kvh) << LOG2_BS) + (t & bmask)) * HD + 8 * col) * 2;
     __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)src,
                                      (void __attribute__((address_space(3))) *)(st + s * kWave), 16, 0,
                                      kMultiLoadPolicy);
   }
 }
 
-// s_waitcnt immediate for vmcnt(n) and lgkmcnt(0) (expcnt left alone).
-__host__ __device__ constexpr int vmcnt_lgkm0(int n) { return (n & 15) | ((n >> 4) << 14) | 0x0070; }
 
 // Until at most `ahead` (0 .. R - 4) later groups of this wave's staging
 // loads (SPW each) are in flight, and every LDS read of this wave has
@@ -1759,14 +1836,25 @@ __device__ __forceinline__ void multi_raw(float (&raw)[16], const f32x16_t &sacc
 }
 
 // V of one staged group, positions past the row end zeroed (they may hold
-// NaN): vc[dt][kk] is hd rows 32 dt .., positions 16 kk + 8 h .. + 8.
+// NaN): vc[dt][kk] is hd rows 32 dt .., positions 16 kk + 8 h .. + 8.  In
+// each 16 lanes, lanes 4r + q read row 16 kk + 8 h + r (then r + 4), hd
+// 32 dt + 16 ((lane / 16) % 2) + 4 q .. + 3; lane i gets hd .. + i.
 template <int HD>
 __device__ __forceinline__ void multi_v(bf16x8_t (&vc)[HD / 32][2], const uint4 *buf, int gbase, int n, int lane) {
   constexpr int KS = HD / 16, DT = HD / 32;
+  const void *vt = buf + KS * kWave;
+  const int i16 = lane & 15, r = i16 >> 2, q = i16 & 3, h = lane >> 5, hs = (lane >> 4) & 1;
 #pragma unroll
-  for (int dt = 0; dt < DT; ++dt)
+  for (int kk = 0; kk < 2; ++kk) {
+    const int p = 16 * kk + 8 * h + r;
+    const uint32_t off = (uint32_t)(p * 2 * HD + 16 * ((2 * hs + (q >> 1)) ^ vswz32<HD>(p)) + 8 * (q & 1));
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) vc[dt][kk] = __builtin_bit_cast(bf16x8_t, buf[(KS + 2 * dt + kk) * kWave + lane]);
+    for (int dt = 0; dt < DT; ++dt) {
+      const uint32_t o = off ^ (uint32_t)(64 * dt);
+      const uint2 lo = lds_read_tr16(vt, o), hi = lds_read_tr16(vt, o + 8 * HD);
+      vc[dt][kk] = __builtin_bit_cast(bf16x8_t, make_uint4(lo.x, lo.y, hi.x, hi.y));
+    }
+  }
   if (gbase + kGroupPositions > n) {
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {

@@ -35,7 +35,7 @@ def gathered_rect_read(q, k_pool, v_pool, block_table, context_lens, scale, widt
     blk = torch.where(live, blk, torch.zeros_like(blk))
     off = torch.where(live, off, torch.zeros_like(off))
     K = k_pool[blk, :, off, :].float()  # [rows, W, nkv, hd]
-    V = v_pool[blk, :, :, off].float()  # V pool is [nb, nkv, hd, bs]
+    V = v_pool[blk, :, off, :].float()  # [rows, W, nkv, hd]
     K = torch.where(live[:, :, None, None], K, torch.zeros_like(K))
     V = torch.where(live[:, :, None, None], V, torch.zeros_like(V))
     qf = q.float().reshape(rows, nkv, G, hd)

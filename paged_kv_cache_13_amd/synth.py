@@ -145,7 +145,7 @@ class DecodeBatch:
     cfg: DecodeConfig
     q: torch.Tensor             # [rows, n_heads, head_dim]
     k_pool: torch.Tensor        # [num_blocks, n_kv_heads, block_size, head_dim]
-    v_pool: torch.Tensor        # [num_blocks, n_kv_heads, head_dim, block_size]
+    v_pool: torch.Tensor        # [num_blocks, n_kv_heads, block_size, head_dim]
     block_table: torch.Tensor   # [rows, max_blocks_per_row] int32
     context_lens: torch.Tensor  # [rows] int32
     ctx_host: np.ndarray        # host copy of the lengths (drawn here, never read back)
@@ -204,7 +204,7 @@ def make_batch(cfg: DecodeConfig, device="cpu", seed: Optional[int] = None,
     gen.manual_seed(seed)
     q = _fill_normal((cfg.rows, cfg.n_heads, cfg.head_dim), dt, device, gen, cfg.value_scale)
     k_pool = _fill_normal((nb, cfg.n_kv_heads, bs, cfg.head_dim), dt, device, gen, cfg.value_scale)
-    v_pool = _fill_normal((nb, cfg.n_kv_heads, cfg.head_dim, bs), dt, device, gen, cfg.value_scale)
+    v_pool = _fill_normal((nb, cfg.n_kv_heads, bs, cfg.head_dim), dt, device, gen, cfg.value_scale)
     if poison:
         unused = np.ones((nb, bs), dtype=bool)
         unused[owned] = False
@@ -214,7 +214,7 @@ def make_batch(cfg: DecodeConfig, device="cpu", seed: Optional[int] = None,
                 unused[table[r, need[r] - 1], n % bs:] = True
         mask = torch.from_numpy(unused).to(device)
         k_pool.masked_fill_(mask[:, None, :, None], float("nan"))
-        v_pool.masked_fill_(mask[:, None, None, :], float("nan"))
+        v_pool.masked_fill_(mask[:, None, :, None], float("nan"))
     return DecodeBatch(cfg=cfg, q=q, k_pool=k_pool, v_pool=v_pool,
                        block_table=torch.from_numpy(table).to(device),
                        context_lens=torch.from_numpy(lens).to(device),
@@ -251,7 +251,7 @@ class DecodeRun:
         self.poison_block = self.alloc.allocate()
         self.k_pool = torch.full((self.num_blocks, n_kv_heads, block_size, head_dim), float("nan"),
                                  dtype=self.dtype, device=device)
-        self.v_pool = torch.full((self.num_blocks, n_kv_heads, head_dim, block_size), float("nan"),
+        self.v_pool = torch.full((self.num_blocks, n_kv_heads, block_size, head_dim), float("nan"),
                                  dtype=self.dtype, device=device)
         self.table_host = np.full((rows, self.max_blocks_per_row), self.poison_block,
                                   dtype=np.int32)

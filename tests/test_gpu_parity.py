@@ -56,7 +56,7 @@ def test_scatter_is_bit_exact(dtype, hd, bs, nkv):
     slots = rng.choice(nb * bs, size=T, replace=False).astype(np.int64)
     slots[rng.choice(T, size=17, replace=False)] = -1
     kp = bits((nb, nkv, bs, hd)).view(tdt)
-    vp = bits((nb, nkv, hd, bs)).view(tdt)
+    vp = bits((nb, nkv, bs, hd)).view(tdt)
     kp_d, vp_d = kp.to(DEV), vp.to(DEV)
     pkv.reshape_and_cache(k.to(DEV), v.to(DEV), torch.from_numpy(slots).to(DEV), kp_d, vp_d)
     torch.cuda.synchronize()
@@ -97,7 +97,7 @@ def test_scatter_many_tokens_is_bit_exact(dtype, hd, bs, nkv, layout):
     far = rng.choice(T, size=5, replace=False)
     slots[far] = nb * bs + np.arange(5)  # outside the pool: skipped by the kernel
     kp = bits((nb, nkv, bs, hd)).view(tdt)
-    vp = bits((nb, nkv, hd, bs)).view(tdt)
+    vp = bits((nb, nkv, bs, hd)).view(tdt)
     kp_d, vp_d = kp.to(DEV), vp.to(DEV)
     pkv.reshape_and_cache(k.to(DEV), v.to(DEV), torch.from_numpy(slots).to(DEV), kp_d, vp_d)
     torch.cuda.synchronize()
@@ -207,7 +207,7 @@ def test_read_edge_lengths(bs):
     assert_close(got, ref, what="edge lengths", **TOL[torch.float32])
     assert np.array_equal(got[0], np.zeros_like(got[0]))  # empty row reads zeros
     # one position: softmax weight exactly 1, output is that V row exactly
-    v0 = b.v_pool[int(b.table_host[1, 0]), :, :, 0].cpu().numpy()
+    v0 = b.v_pool[int(b.table_host[1, 0]), :, 0, :].cpu().numpy()
     assert np.array_equal(got[1], np.repeat(v0, 4, axis=0))
 
 
@@ -430,7 +430,7 @@ def test_read_constant_values_give_that_constant(dtype, hd, width):
                     max_ctx=width or None)
     b = synth.make_batch(cfg, device=DEV)
     c = torch.linspace(-2, 2, hd, device=DEV).to(b.v_pool.dtype)  # exact in bf16
-    b.v_pool.copy_(c[None, None, :, None].expand_as(b.v_pool))
+    b.v_pool.copy_(c[None, None, None, :].expand_as(b.v_pool))
     got = gpu_read(b, out_dtype=torch.float32).cpu()
     expect = c.float().cpu()[None, None, :].expand_as(got)
     assert_close(got, expect, what="constant V", atol=1e-6, rtol=1e-5)
@@ -699,7 +699,7 @@ def test_pool_churn_under_scatter_and_read():
     nb = 90  # well under rows * width_blocks: blocks are reused and the pool runs dry
     alloc = pkv.BlockAllocator(nb, seed=17)
     k_pool = torch.full((nb, KV, bs, hd), float("nan"), dtype=torch.bfloat16, device=DEV)
-    v_pool = torch.full((nb, KV, hd, bs), float("nan"), dtype=torch.bfloat16, device=DEV)
+    v_pool = torch.full((nb, KV, bs, hd), float("nan"), dtype=torch.bfloat16, device=DEV)
     tables = np.full((rows, width_blocks), -1, dtype=np.int32)
     lens = np.zeros(rows, dtype=np.int32)
     g = torch.Generator(device=DEV).manual_seed(4)

@@ -29,19 +29,12 @@ def small_cfg(name="t", dtype="f32", rows=3, H=4, KV=2, hd=16, bs=8, lo=1, hi=80
 
 
 def assembled_history(pool, table_row, n, bs):
-    """Row history [n, n_kv, hd] read with numpy's view of the K pool layout
-    [num_blocks, n_kv, block_size, hd] -- indexing, transpose and reshape only."""
+    """Row history [n, n_kv, hd] read with numpy's view of the pool layout
+    [num_blocks, n_kv, block_size, hd] (K and V alike) -- indexing, transpose
+    and reshape only."""
     need = -(-n // bs)
     blocks = pool[np.asarray(table_row[:need], dtype=np.int64)]      # [need, n_kv, bs, hd]
     return blocks.transpose(0, 2, 1, 3).reshape(need * bs, pool.shape[1], pool.shape[3])[:n]
-
-
-def assembled_history_v(pool, table_row, n, bs):
-    """Row history [n, n_kv, hd] read with numpy's view of the V pool layout
-    [num_blocks, n_kv, hd, block_size] (dimension-major inside a block)."""
-    need = -(-n // bs)
-    blocks = pool[np.asarray(table_row[:need], dtype=np.int64)]      # [need, n_kv, hd, bs]
-    return blocks.transpose(0, 3, 1, 2).reshape(need * bs, pool.shape[1], pool.shape[2])[:n]
 
 
 def sdpa_reference(batch):
@@ -57,7 +50,7 @@ def sdpa_reference(batch):
         if n == 0:
             continue
         K = torch.from_numpy(assembled_history(kp, batch.table_host[r], n, cfg.block_size))
-        V = torch.from_numpy(assembled_history_v(vp, batch.table_host[r], n, cfg.block_size))
+        V = torch.from_numpy(assembled_history(vp, batch.table_host[r], n, cfg.block_size))
         K = K.permute(1, 0, 2).repeat_interleave(G, dim=0)  # [H, n, hd]
         V = V.permute(1, 0, 2).repeat_interleave(G, dim=0)
         o = torch.nn.functional.scaled_dot_product_attention(
@@ -110,7 +103,7 @@ def test_single_position_returns_that_value_exactly():
     got = run_oracle(b)
     vp = b.v_pool.to(torch.float64).numpy()
     for r in range(cfg.rows):
-        v0 = vp[b.table_host[r, 0], :, :, 0]  # [n_kv, hd]
+        v0 = vp[b.table_host[r, 0], :, 0, :]  # [n_kv, hd]
         expect = np.repeat(v0, cfg.n_heads // cfg.n_kv_heads, axis=0)
         assert np.array_equal(got[r], expect)
 
@@ -122,7 +115,7 @@ def test_zero_query_gives_mean_of_values():
     got = run_oracle(b)
     vp = b.v_pool.to(torch.float64).numpy()
     for r in range(cfg.rows):
-        V = assembled_history_v(vp, b.table_host[r], int(b.ctx_host[r]), cfg.block_size)
+        V = assembled_history(vp, b.table_host[r], int(b.ctx_host[r]), cfg.block_size)
         expect = np.repeat(V.mean(axis=0), 2, axis=0)
         np.testing.assert_allclose(got[r], expect, rtol=1e-13, atol=1e-14)
 
@@ -131,7 +124,7 @@ def test_constant_values_give_that_constant():
     cfg = small_cfg("cv", "f32", rows=2, H=4, KV=2, hd=16, bs=8, lo=3, hi=60)
     b = synth.make_batch(cfg, poison=False)
     c = torch.randn(cfg.n_kv_heads, cfg.head_dim, generator=torch.Generator().manual_seed(3))
-    b.v_pool[:] = c[None, :, :, None]
+    b.v_pool[:] = c[None, :, None, :]
     got = run_oracle(b)
     expect = np.repeat(c.double().numpy(), 2, axis=0)
     for r in range(cfg.rows):
@@ -154,7 +147,7 @@ def test_one_dominant_key_selects_its_value():
         n = int(b.ctx_host[r])
         star = (7 * r + 3) % n
         K = assembled_history(kp, b.table_host[r], n, cfg.block_size)[:, 0]
-        V = assembled_history_v(vp, b.table_host[r], n, cfg.block_size)[:, 0]
+        V = assembled_history(vp, b.table_host[r], n, cfg.block_size)[:, 0]
         s = 40.0 * K @ K[star].astype(np.float32).astype(np.float64)
         margin = s[star] - np.max(np.delete(s, star))
         assert margin > 50
@@ -202,19 +195,19 @@ def test_reblocking_same_history_is_bitwise_invariant():
     mb = -(-cfg8.max_ctx // bs32)
     nb = cfg8.rows * mb
     kp32 = np.full((nb, cfg8.n_kv_heads, bs32, cfg8.head_dim), np.nan, dtype=np.float32)
-    vp32 = np.full((nb, cfg8.n_kv_heads, cfg8.head_dim, bs32), np.nan, dtype=np.float32)
+    vp32 = np.full((nb, cfg8.n_kv_heads, bs32, cfg8.head_dim), np.nan, dtype=np.float32)
     table32 = np.zeros((cfg8.rows, mb), dtype=np.int32)
     for r in range(cfg8.rows):
         n = int(b8.ctx_host[r])
         K = assembled_history(kp, b8.table_host[r], n, 8)
-        V = assembled_history_v(vp, b8.table_host[r], n, 8)
+        V = assembled_history(vp, b8.table_host[r], n, 8)
         for j in range(-(-n // bs32)):
             blk = r * mb + j
             table32[r, j] = blk
             seg = slice(j * bs32, min(n, (j + 1) * bs32))
             w = seg.stop - seg.start
             kp32[blk, :, :w, :] = K[seg].transpose(1, 0, 2)
-            vp32[blk, :, :, :w] = V[seg].transpose(1, 2, 0)
+            vp32[blk, :, :w, :] = V[seg].transpose(1, 0, 2)
     got = run_oracle(b8, k_pool=kp32, v_pool=vp32, block_table=table32)
     assert np.array_equal(run_oracle(b8), got)
 
@@ -273,15 +266,9 @@ def test_streamed_tile_walk_equals_gathered_read(cfg, tile):
 # ---------------------------------------------------------------------------
 
 def _slot_view(pool):
-    """[num_blocks * block_size, n_kv, hd] view of a [nb, n_kv, bs, hd] K pool."""
+    """[num_blocks * block_size, n_kv, hd] view of a [nb, n_kv, bs, hd] pool."""
     nb, nkv, bs, hd = pool.shape
     return pool.transpose(0, 2, 1, 3).reshape(nb * bs, nkv, hd)
-
-
-def _slot_view_v(pool):
-    """[num_blocks * block_size, n_kv, hd] view of a [nb, n_kv, hd, bs] V pool."""
-    nb, nkv, hd, bs = pool.shape
-    return pool.transpose(0, 3, 1, 2).reshape(nb * bs, nkv, hd)
 
 
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
@@ -297,16 +284,15 @@ def test_scatter_round_trip_is_bit_exact(dtype):
     slots[[3, 17]] = -1  # padding tokens are skipped
     fill = np.full((nb, nkv, bs, hd), 0x7F7F7F7F if dtype == "f32" else 0x7F7F,
                    dtype=word).view(npdt)
-    fill_v = np.ascontiguousarray(fill.transpose(0, 1, 3, 2))
-    kp, vp = fill.copy(), fill_v.copy()
+    kp, vp = fill.copy(), fill.copy()
     oracle.reshape_and_cache(k, v, slots, kp, vp)
-    ks, vs = _slot_view(kp), _slot_view_v(vp)
+    ks, vs = _slot_view(kp), _slot_view(vp)
     live = slots >= 0
     assert ks[slots[live]].tobytes() == k[live].tobytes()
     assert vs[slots[live]].tobytes() == v[live].tobytes()
     untouched = np.setdiff1d(np.arange(nb * bs), slots[live])
     assert ks[untouched].tobytes() == _slot_view(fill)[untouched].tobytes()
-    assert vs[untouched].tobytes() == _slot_view_v(fill_v)[untouched].tobytes()
+    assert vs[untouched].tobytes() == _slot_view(fill)[untouched].tobytes()
 
 
 def test_scatter_then_read_equals_read_of_the_history():
@@ -320,7 +306,7 @@ def test_scatter_then_read_equals_read_of_the_history():
     blocks = rng.permutation(nb)[: -(-n // bs)]
     slots = (blocks[np.arange(n) // bs] * bs + np.arange(n) % bs).astype(np.int64)
     kp = np.full((nb, KV, bs, hd), np.nan, dtype=np.float32)
-    vp = np.full((nb, KV, hd, bs), np.nan, dtype=np.float32)
+    vp = np.full((nb, KV, bs, hd), np.nan, dtype=np.float32)
     oracle.reshape_and_cache(K, V, slots, kp, vp)
     table = np.zeros((1, -(-n // bs)), dtype=np.int32)
     table[0] = blocks
@@ -335,7 +321,7 @@ def test_scatter_then_read_equals_read_of_the_history():
 def test_scatter_rejects_out_of_pool_slot():
     k = np.zeros((1, 1, 16), dtype=np.float32)
     kp = np.zeros((2, 1, 8, 16), dtype=np.float32)
-    vp = np.zeros((2, 1, 16, 8), dtype=np.float32)
+    vp = np.zeros((2, 1, 8, 16), dtype=np.float32)
     with pytest.raises(RuntimeError):
         oracle.reshape_and_cache(k, k.copy(), np.array([16], dtype=np.int64), kp, vp)
 
@@ -370,7 +356,7 @@ def decode_run_cells(rows, widths, block, heads=8, layers=2, seed=0):
         need = -(-w // bs)
         nb = rows * need
         kp = rng.standard_normal((nb, kv, bs, hd)).astype(np.float32)
-        vp = rng.standard_normal((nb, kv, hd, bs)).astype(np.float32)
+        vp = rng.standard_normal((nb, kv, bs, hd)).astype(np.float32)
         table = rng.permutation(nb).astype(np.int32).reshape(rows, need)
         lens = np.full(rows, w, dtype=np.int32)
         slots = np.stack([(table[r][np.arange(w) // bs] * bs + np.arange(w) % bs) for r in range(rows)])
@@ -412,7 +398,7 @@ def test_fixed_shape_saving_is_width_over_block(w, block):
     lens = np.full(rows, w, dtype=np.int32)
     slots = np.stack([table[r][np.arange(w) // bs] * bs + np.arange(w) % bs for r in range(rows)])
     q = rng.standard_normal((rows, heads, hd)).astype(np.float32)
-    vp = np.ascontiguousarray(kp.transpose(0, 1, 3, 2))
+    vp = kp.copy()
     _, charged = oracle.paged_attention_slots(q, kp, vp, slots, lens, 1.0)
     _, held = oracle.paged_attention_streamed(q, kp, vp, table, lens, 1.0, block)
     assert Fraction(charged, held) == Fraction(w, block)
@@ -443,7 +429,7 @@ def causal_sdpa_reference(b, q):
         if n == 0:
             continue
         K = torch.from_numpy(assembled_history(kp, b.table_host[r], n, cfg.block_size))
-        V = torch.from_numpy(assembled_history_v(vp, b.table_host[r], n, cfg.block_size))
+        V = torch.from_numpy(assembled_history(vp, b.table_host[r], n, cfg.block_size))
         K = K.permute(1, 0, 2).repeat_interleave(G, dim=0).contiguous()  # [H, n, hd]
         V = V.permute(1, 0, 2).repeat_interleave(G, dim=0).contiguous()
         pos = torch.arange(n)[None, :]

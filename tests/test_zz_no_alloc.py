@@ -56,7 +56,7 @@ def test_noalloc_read_refuses_a_read_larger_than_its_buffer():
     cfg = synth.CONFIGS["llama3_8b_layer"]
     q = torch.zeros(8192, cfg.n_heads, cfg.head_dim, dtype=torch.float32, device=DEV)
     kp = torch.zeros(4, cfg.n_kv_heads, cfg.block_size, cfg.head_dim, dtype=torch.float32, device=DEV)
-    vp = torch.zeros(4, cfg.n_kv_heads, cfg.head_dim, cfg.block_size, dtype=torch.float32, device=DEV)
+    vp = torch.zeros(4, cfg.n_kv_heads, cfg.block_size, cfg.head_dim, dtype=torch.float32, device=DEV)
     bt = torch.zeros(8192, 256, dtype=torch.int32, device=DEV)
     cl = torch.zeros(8192, dtype=torch.int32, device=DEV)
     assert pkv.workspace_size(q, kp, bt) > 32 << 20
