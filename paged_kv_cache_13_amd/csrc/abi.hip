@@ -19,7 +19,7 @@ constexpr int32_t kDefaultPartition = 512;
 constexpr int64_t kTargetWorkgroups = 512;
 constexpr int32_t kStreamMinGroups = 4;  // 128 positions
 constexpr int32_t kMaxGroup = 16;
-constexpr int32_t kMaxPartitionBlocks = 4096;  // LDS holds one partition's block ids (16 KB)
+using pkv::kMaxPartitionBlocks;  // LDS holds one partition's block ids (16 KB)
 
 bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0; }
 bool dtype_ok(int32_t d) { return d == PKV_F32 || d == PKV_BF16; }

@@ -175,6 +175,42 @@ __device__ __forceinline__ WorkItem work_item(const DecodeArgs &a) {
   return w;
 }
 
+// Partition kernels: the partition's block ids, every entry up to the
+// table's width whatever the row's length, loaded by thread tid (entries
+// tid, tid + kThreads, ...) together with the row's length, so that the
+// length and the ids cost one round trip, not two.  Entries past the row's
+// blocks are loaded and never used.
+constexpr int kIdsPerThread = kMaxPartitionBlocks / kThreads;
+struct PartIds {
+  int32_t v[kIdsPerThread];
+};
+__device__ __forceinline__ int part_ids_count(const DecodeArgs &a, int start) {
+  const int cap = a.max_blocks_per_row * a.block_size;
+  return (min(start + a.partition_tokens, cap) - start + a.block_size - 1) >> a.log2_bs;
+}
+__device__ __forceinline__ void part_ids_load(PartIds &ids, const DecodeArgs &a, int r, int start, int tid) {
+  const int cnt = part_ids_count(a, start);
+  const int32_t *row = a.block_table + (size_t)r * a.max_blocks_per_row + (start >> a.log2_bs);
+#pragma unroll
+  for (int x = 0; x < kIdsPerThread; ++x) {
+    const int i = tid + x * kThreads;
+    ids.v[x] = i < cnt ? row[i] : 0;
+  }
+}
+// The ids, clamped into the pool, to LDS (the caller's barrier publishes them).
+__device__ __forceinline__ void part_ids_store(const PartIds &ids, const DecodeArgs &a, int start, int tid,
+                                               int32_t *s_blk) {
+  const int cnt = part_ids_count(a, start);
+#pragma unroll
+  for (int x = 0; x < kIdsPerThread; ++x) {
+    const int i = tid + x * kThreads;
+    if (i < cnt) {
+      const int64_t b = ids.v[x];
+      s_blk[i] = (int32_t)(b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b));
+    }
+  }
+}
+
 // Partition kernels: one kv head's new token of row r, stored into its pool
 // slot by threads t0, t0 + nthreads, ... (skipped like the scatter skips).
 // E: the pool's element type, bit-copied.
@@ -221,10 +257,12 @@ __global__ __launch_bounds__(kThreads) void decode_partition(DecodeArgs a) {
   const int p = it.p, g = it.g, r = it.r;
   const int tid = threadIdx.x;
   const int cap = a.max_blocks_per_row * a.block_size;
-  int n = a.context_lens[r];
-  n = n < 0 ? 0 : (n > cap ? cap : n);
   const int P = a.partition_tokens;
   const int start = p * P;
+  int n = a.context_lens[r];
+  PartIds pids;
+  part_ids_load(pids, a, r, start, tid);
+  n = n < 0 ? 0 : (n > cap ? cap : n);
   const int group = a.group;
   if (start >= n) {
     if (p == 0) {  // empty row: zeros
@@ -239,15 +277,7 @@ __global__ __launch_bounds__(kThreads) void decode_partition(DecodeArgs a) {
   const int end = min(n, start + P);
   const bool single = n <= P;
 
-  // This partition's block ids, clamped into the pool.
-  const int nblk = (end - start + a.block_size - 1) >> a.log2_bs;
-  const int first_blk = start >> a.log2_bs;
-  const int32_t *table_row = a.block_table + (size_t)r * a.max_blocks_per_row + first_blk;
-  for (int i = tid; i < nblk; i += kThreads) {
-    int64_t b = table_row[i];
-    b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
-    s_blk[i] = (int32_t)b;
-  }
+  part_ids_store(pids, a, start, tid, s_blk);  // this partition's block ids, clamped into the pool
 
   const int lane = tid % kWave;
   const int wave = tid / kWave;
@@ -395,6 +425,9 @@ __global__ __launch_bounds__(kThreads) void decode_partition(DecodeArgs a) {
 // Merge of the partitions of rows that span more than one:
 //   M = max_p m_p;  L = sum_p l_p 2^(m_p - M);  out = sum_p acc_p 2^(m_p - M) / L
 // (m_p in the log2 domain).  Rows with one partition were written directly.
+// The partials of up to kMergeBatch partitions are loaded together (one
+// round trip per batch, not one per partition), then folded in order.
+constexpr int kMergeBatch = 8;
 __global__ __launch_bounds__(128) void decode_merge(DecodeArgs a) {
   const int r = blockIdx.x / a.n_heads;
   const int h = blockIdx.x % a.n_heads;
@@ -409,15 +442,34 @@ __global__ __launch_bounds__(128) void decode_merge(DecodeArgs a) {
   const float *mp = a.ws + ws.m_off + base;
   const float *lp = a.ws + ws.l_off + base;
   const float *ap = a.ws + ws.acc_off + base * a.head_dim;
-  float M = -INFINITY;
-  for (int p = 0; p < nparts; ++p) M = fmaxf(M, mp[p]);
-  float L = 0.f;
-  for (int p = 0; p < nparts; ++p) L = fmaf(lp[p], exp2_fast(mp[p] - M), L);
-  const float inv = 1.f / L;
-  for (int d = threadIdx.x; d < a.head_dim; d += blockDim.x) {
-    float O = 0.f;
-    for (int p = 0; p < nparts; ++p) O = fmaf(ap[(size_t)p * a.head_dim + d], exp2_fast(mp[p] - M), O);
-    store_out(a.out, a.out_dtype, ((size_t)r * a.n_heads + h) * a.head_dim + d, O * inv);
+  for (int d0 = 0; d0 < a.head_dim; d0 += blockDim.x) {
+    const int d = d0 + (int)threadIdx.x;
+    const bool live = d < a.head_dim;
+    float M = -INFINITY, L = 0.f, O = 0.f;
+    for (int p0 = 0; p0 < nparts; p0 += kMergeBatch) {
+      float mk[kMergeBatch], lk[kMergeBatch], ak[kMergeBatch];
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) {
+        const bool in = p0 + k < nparts;
+        mk[k] = in ? mp[p0 + k] : -INFINITY;
+        lk[k] = in ? lp[p0 + k] : 0.f;
+        ak[k] = in && live ? ap[(size_t)(p0 + k) * a.head_dim + d] : 0.f;
+      }
+      float mn = M;
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) mn = fmaxf(mn, mk[k]);
+      const float a0 = M == -INFINITY ? 0.f : exp2_fast(M - mn);
+      L *= a0;
+      O *= a0;
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k) {
+        const float wk = mk[k] == -INFINITY ? 0.f : exp2_fast(mk[k] - mn);
+        L = fmaf(lk[k], wk, L);
+        O = fmaf(ak[k], wk, O);
+      }
+      M = mn;
+    }
+    if (live) store_out(a.out, a.out_dtype, ((size_t)r * a.n_heads + h) * a.head_dim + d, O / L);
   }
 }
 
@@ -794,10 +846,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int p = it.p, g = it.g, r = it.r;
   const int tid = threadIdx.x;
   const int cap = a.max_blocks_per_row * a.block_size;
-  int n = a.context_lens[r];
-  n = n < 0 ? 0 : (n > cap ? cap : n);
   const int P = a.partition_tokens;
   const int start = p * P;
+  int n = a.context_lens[r];
+  PartIds pids;
+  part_ids_load(pids, a, r, start, tid);
+  n = n < 0 ? 0 : (n > cap ? cap : n);
   const int group = a.group;
   if (start >= n) {
     if (p == 0) {
@@ -824,13 +878,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const bool tok_wave = a.slot_new != nullptr && n - 1 < end && ((n - 1 - start) / GT) % kWaves == wave;
   TokenRow<HD> tok;
   if (tok_wave) token_fetch<HD>(tok, a, r, g, lane);
-  const int nblk = (end - start + a.block_size - 1) >> a.log2_bs;
-  const int32_t *table_row = a.block_table + (size_t)r * a.max_blocks_per_row + (start >> a.log2_bs);
-  for (int i = tid; i < nblk; i += kThreads) {
-    int64_t b = table_row[i];
-    b = b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b);
-    s_blk[i] = (int32_t)b;
-  }
+  part_ids_store(pids, a, start, tid, s_blk);
 
   bf16x8_t qb[KS];
 #pragma unroll

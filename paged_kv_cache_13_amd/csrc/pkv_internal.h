@@ -48,6 +48,7 @@ __host__ __device__ inline int32_t multi_waves(int32_t tiles) { return tiles > 4
 // two workgroups share one.
 __host__ __device__ constexpr int multi_ring(int waves) { return waves >= 8 ? 8 : 4; }
 constexpr int kMultiMaxPartition = 4096;   // positions per multi-query partition, at most
+constexpr int32_t kMaxPartitionBlocks = 4096;  // block ids of one partition of the partition kernels, at most
 
 // Workspace of the split-context read, in floats: running max m and sum l
 // per (row, query head, partition), then the fp32 partial output rows.
