@@ -176,9 +176,20 @@ int plan_decode(const pkv_attn_desc *d, Plan *pl) {
 //   64 rows x  8 queries  205.2 / 176.2 / 158.9* / 171.1
 constexpr int64_t kComputeUnits = 256;
 constexpr int64_t kStreamMultiGroups = 32;
+// Balanced multi-query read (one query block per (row, kv head), at most
+// kWindowRows rows): slices of at least this many 32-position groups by
+// default (the caller's partition_tokens, rounded up to whole groups,
+// replaces it), one per persistent workgroup.
+constexpr int64_t kMultiSliceMinGroups = 16;
+// ... and only for at least this many (row, kv head) pairs: below, the
+// partition kernel's workgroups start at once and the balanced read's fixed
+// costs do not pay (8B shape, 64 queries: 4 rows 44.8 vs 49.5 us, 8 rows
+// 62.5 vs 63.6; 16 rows 97.1 vs 90.3, 64 rows 321.4 vs 265.9).
+constexpr int64_t kMultiBalancedMinPairs = 128;
 struct MultiPlan {
   int32_t q_tiles, q_per_tile, q_blocks;
   int32_t stream;  // 1: query_len * group <= 16 columns on the stream path
+  int32_t stream_waves;  // balanced multi-query read: persistent workgroups
 };
 int plan_multi(const pkv_attn_desc *d, int32_t query_len, Plan *pl, MultiPlan *mp) {
   if (!d) return PKV_ERR_NULL;
@@ -217,12 +228,28 @@ int plan_multi(const pkv_attn_desc *d, int32_t query_len, Plan *pl, MultiPlan *m
   const int32_t waves = pkv::multi_waves(mp->q_tiles);
   mp->q_blocks = (mp->q_tiles + waves - 1) / waves;
   const int64_t g32 = pkv::kGroupPositions;
+  const int64_t per_cu = std::max<int64_t>(1, (d->head_dim == 128 ? 4 : 8) / waves);  // registers, LDS
+  mp->stream_waves = 0;
+  if (mp->q_blocks == 1 && d->rows <= pkv::kWindowRows &&
+      (int64_t)d->rows * d->n_kv_heads >= kMultiBalancedMinPairs) {
+    // balanced: one slice of the (kv head, row) group stream per persistent
+    // workgroup, as many workgroups as the GPU holds at once
+    mp->stream_waves = (int32_t)(kComputeUnits * per_cu);
+    pl->stream = 2;
+    pl->cg_min = (int32_t)(d->partition_tokens ? (d->partition_tokens + g32 - 1) / g32 : kMultiSliceMinGroups);
+    pl->partition = 0;
+    pl->max_parts = 0;
+    if ((int64_t)d->rows * query_len * d->n_heads > INT_MAX) return PKV_ERR_SHAPE;
+    pl->ws_bytes = d->rows > 0 ? pkv::stream_layout(d->rows, query_len * pl->group, d->head_dim, mp->stream_waves).total *
+                                     sizeof(int32_t)
+                               : 0;
+    return PKV_OK;
+  }
   int64_t part;
   if (d->partition_tokens) {
     part = (d->partition_tokens + g32 - 1) / g32 * g32;
   } else {
     const int64_t blocks = (int64_t)mp->q_blocks * d->n_kv_heads * (d->rows > 0 ? d->rows : 1);
-    const int64_t per_cu = std::max<int64_t>(1, (d->head_dim == 128 ? 4 : 8) / waves);  // registers, LDS
     const int64_t want = (int64_t)cap * blocks / (kComputeUnits * per_cu);
     // two-wave workgroups (at most two tiles) stop at 1024 positions
     const int64_t top = waves <= 2 ? 1024 : 2048;
@@ -300,6 +327,7 @@ int launch_attention(const pkv_attn_desc *d, const Plan &pl, const void *q, cons
   a.max_parts = pl.max_parts;
   a.stream = pl.stream;
   a.cg_min = pl.cg_min;
+  a.stream_waves = pkv::kStreamWaves;
   a.inplan = pl.stream && d->rows <= pkv::kWindowRows;
   a.num_blocks = d->num_blocks;
   a.dtype = d->dtype;
@@ -496,6 +524,7 @@ int pkv_paged_attention_multi(const pkv_attn_desc *d, int32_t query_len, const v
     a.max_parts = pl.max_parts;
     a.stream = 1;
     a.cg_min = pl.cg_min;
+    a.stream_waves = pkv::kStreamWaves;
     a.inplan = d->rows <= pkv::kWindowRows;
     a.num_blocks = d->num_blocks;
     a.dtype = d->dtype;
@@ -531,6 +560,10 @@ int pkv_paged_attention_multi(const pkv_attn_desc *d, int32_t query_len, const v
   a.q_tiles = mp.q_tiles;
   a.q_per_tile = mp.q_per_tile;
   a.q_blocks = mp.q_blocks;
+  a.stream = pl.stream;  // 2: the balanced multi-query read
+  a.cg_min = pl.cg_min;
+  a.stream_waves = mp.stream_waves;
+  a.cols = query_len * pl.group;
   return pkv::launch_multi(a, static_cast<hipStream_t>(stream)) == hipSuccess ? PKV_OK : PKV_ERR_LAUNCH;
 }
 

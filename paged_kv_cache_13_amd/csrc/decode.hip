@@ -1012,7 +1012,7 @@ __global__ __launch_bounds__(1024) void decode_plan(DecodeArgs a) {
   const int tid = threadIdx.x;
   const int rows = a.rows;
   const int cap = a.max_blocks_per_row * a.block_size;
-  const StreamLayout L = stream_layout(rows, a.cols, a.head_dim);
+  const StreamLayout L = stream_layout(rows, a.cols, a.head_dim, a.stream_waves);
   int32_t *wsi = reinterpret_cast<int32_t *>(a.ws);
   const int per = (rows + 1023) / 1024;
   const int r0 = min(rows, tid * per), r1 = min(rows, r0 + per);
@@ -1046,7 +1046,7 @@ __global__ __launch_bounds__(1024) void decode_plan(DecodeArgs a) {
   // differ by at most one group.
   const long long ng_all = (long long)a.n_kv_heads * ngk;
   long long waves = ng_all / max(a.cg_min, 1);
-  waves = waves < 1 ? 1 : (waves > kStreamWaves ? kStreamWaves : waves);
+  waves = waves < 1 ? 1 : (waves > a.stream_waves ? a.stream_waves : waves);
   if (ng_all == 0) waves = 0;
   if (tid == 0) {
     wsi[L.hdr] = ngk;
@@ -1336,7 +1336,7 @@ __device__ __forceinline__ void segment_end(const DecodeArgs &a, const StreamLay
 constexpr int kMergeMaxParts = 8;
 constexpr int kMergeElems = 2;
 __global__ __launch_bounds__(256) void decode_stream_merge(DecodeArgs a) {
-  const StreamLayout L = stream_layout(a.rows, a.cols, a.head_dim);
+  const StreamLayout L = stream_layout(a.rows, a.cols, a.head_dim, a.stream_waves);
   const int32_t *wsi = reinterpret_cast<const int32_t *>(a.ws);
   const int pair = blockIdx.x;
   const int kvh = pair / a.rows, r = pair - kvh * a.rows;
@@ -1369,7 +1369,7 @@ __global__ __launch_bounds__(256) void decode_stream_merge(DecodeArgs a) {
     ng = (s_len + kGroupPositions - 1) / kGroupPositions;
     const long long all = (long long)a.n_kv_heads * ngk;
     waves = all / max(a.cg_min, 1);
-    waves = waves < 1 ? 1 : (waves > kStreamWaves ? kStreamWaves : waves);
+    waves = waves < 1 ? 1 : (waves > a.stream_waves ? a.stream_waves : waves);
   } else {
     ngk = wsi[L.hdr];
     waves = wsi[L.hdr + 1];
@@ -1524,7 +1524,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
   __shared__ uint4 s_k[2 * KS * kWave];
   __shared__ uint4 s_v[DT * kWave];
   __shared__ int32_t s_wctx[kWindowRows], s_wgpre[kWindowRows];
-  const StreamLayout L = stream_layout(a.rows, a.cols, a.head_dim);
+  const StreamLayout L = stream_layout(a.rows, a.cols, a.head_dim, a.stream_waves);
   const int32_t *wsi = reinterpret_cast<const int32_t *>(a.ws);
   const int w = blockIdx.x;
   const int lane = threadIdx.x, lr = lane & 15, lg = lane >> 4;
@@ -1543,7 +1543,7 @@ __global__ __launch_bounds__(kWave) __attribute__((amdgpu_waves_per_eu(2))) void
     ngk = plan_in_wave(win, a, lane, cap);
     const long long ng_all0 = (long long)a.n_kv_heads * ngk;
     waves = ng_all0 / max(a.cg_min, 1);
-    waves = waves < 1 ? 1 : (waves > kStreamWaves ? kStreamWaves : waves);
+    waves = waves < 1 ? 1 : (waves > a.stream_waves ? a.stream_waves : waves);
     if (w < a.rows && win.ctx[w] == 0) {  // an empty row reads zeros (all its queries); no slice visits it
       const int per_row = a.query_len * a.n_heads * a.head_dim;
       for (int idx = lane; idx < per_row; idx += kWave)
@@ -2034,6 +2034,61 @@ __device__ __forceinline__ void multi_pair(MultiState<HD> &S, const uint4 *c0, c
   }
 }
 
+// c > 0 for the statistics; a zero scale becomes 1e-30 (every weight still
+// exp2(0) = 1) and a NaN scale stays NaN
+__device__ __forceinline__ float multi_cscale(const DecodeArgs &a) {
+  const float cs = fabsf(a.scale) * kLog2e;
+  return cs < 1e-30f ? 1e-30f : cs;
+}
+
+// Groups g0 .. g0 + ng - 1 of (row, kv head) through the ring: the prologue
+// stages the first R - 2, then the pairs (multi_pair).  s_blk holds the
+// block ids from block blk0 on (nblk of them) and has been published; on
+// return every staged load has been consumed, but other waves may still be
+// reading the ring's last buffers.
+template <int HD, int BS, int NW>
+__device__ __forceinline__ void multi_run(MultiState<HD> &S, uint4 *s_b0, uint4 *s_b1, uint4 *s_b2, uint4 *s_b3,
+                                          uint4 *s_b4, uint4 *s_b5, uint4 *s_b6, uint4 *s_b7, const DecodeArgs &a,
+                                          const int32_t *s_blk, int blk0, int nblk, int kvh, int g0, int ng, int n,
+                                          float cscale, bool active, int wave, int lane) {
+  constexpr int R = multi_ring(NW);
+  const int last = n - 1;
+  auto stage = [&](uint4 *buf, int j) {
+    if (j < ng) stage_multi<HD, BS, NW>(buf, a, s_blk, blk0, nblk, kvh, (g0 + j) * kGroupPositions, last, wave, lane);
+  };
+  stage(s_b0, 0);
+  stage(s_b1, 1);
+  if constexpr (R == 8) {
+    stage(s_b2, 2);
+    stage(s_b3, 3);
+    stage(s_b4, 4);
+    stage(s_b5, 5);
+  }
+  if constexpr (R == 8) {
+    for (int k = 0; k < ng; k += 8) {
+      multi_pair<HD, BS, NW, R>(S, s_b0, s_b1, s_b6, s_b7, a, s_blk, blk0, nblk, kvh, g0, k, ng, n, cscale, active, wave,
+                                lane);
+      if (k + 2 >= ng) break;
+      multi_pair<HD, BS, NW, R>(S, s_b2, s_b3, s_b0, s_b1, a, s_blk, blk0, nblk, kvh, g0, k + 2, ng, n, cscale, active,
+                                wave, lane);
+      if (k + 4 >= ng) break;
+      multi_pair<HD, BS, NW, R>(S, s_b4, s_b5, s_b2, s_b3, a, s_blk, blk0, nblk, kvh, g0, k + 4, ng, n, cscale, active,
+                                wave, lane);
+      if (k + 6 >= ng) break;
+      multi_pair<HD, BS, NW, R>(S, s_b6, s_b7, s_b4, s_b5, a, s_blk, blk0, nblk, kvh, g0, k + 6, ng, n, cscale, active,
+                                wave, lane);
+    }
+  } else {
+    for (int k = 0; k < ng; k += 4) {
+      multi_pair<HD, BS, NW, R>(S, s_b0, s_b1, s_b2, s_b3, a, s_blk, blk0, nblk, kvh, g0, k, ng, n, cscale, active, wave,
+                                lane);
+      if (k + 2 >= ng) break;
+      multi_pair<HD, BS, NW, R>(S, s_b2, s_b3, s_b0, s_b1, a, s_blk, blk0, nblk, kvh, g0, k + 2, ng, n, cscale, active,
+                                wave, lane);
+    }
+  }
+}
+
 template <int HD, int BS, int NW>
 __global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(NW / 4 > 1 ? NW / 4 : 1, 2))) void
 decode_multi(DecodeArgs a) {
@@ -2109,46 +2164,8 @@ decode_multi(DecodeArgs a) {
     for (int j = 0; j < 16; ++j) S.acc[dt][j] = 0.f;
   const bool active = q0 < Q;  // some column of this wave is a query
   __syncthreads();  // s_blk is written
-  const int last = n - 1;
-  // prologue: the first R - 2 groups
-  auto stage = [&](uint4 *buf, int j) {
-    if (j < ng) stage_multi<HD, BS, NW>(buf, a, s_blk, blk0, nblk_all, kvh, (g0 + j) * kGroupPositions, last, wave, lane);
-  };
-  stage(s_b0, 0);
-  stage(s_b1, 1);
-  if constexpr (R == 8) {
-    stage(s_b2, 2);
-    stage(s_b3, 3);
-    stage(s_b4, 4);
-    stage(s_b5, 5);
-  }
-  // c > 0 for the statistics; a zero scale becomes 1e-30 (every weight still
-  // exp2(0) = 1) and a NaN scale stays NaN
-  const float cs = fabsf(a.scale) * kLog2e;
-  const float cscale = cs < 1e-30f ? 1e-30f : cs;
-  if constexpr (R == 8) {
-    for (int k = 0; k < ng; k += 8) {
-      multi_pair<HD, BS, NW, R>(S, s_b0, s_b1, s_b6, s_b7, a, s_blk, blk0, nblk_all, kvh, g0, k, ng, n, cscale, active, wave,
-                                lane);
-      if (k + 2 >= ng) break;
-      multi_pair<HD, BS, NW, R>(S, s_b2, s_b3, s_b0, s_b1, a, s_blk, blk0, nblk_all, kvh, g0, k + 2, ng, n, cscale, active,
-                                wave, lane);
-      if (k + 4 >= ng) break;
-      multi_pair<HD, BS, NW, R>(S, s_b4, s_b5, s_b2, s_b3, a, s_blk, blk0, nblk_all, kvh, g0, k + 4, ng, n, cscale, active,
-                                wave, lane);
-      if (k + 6 >= ng) break;
-      multi_pair<HD, BS, NW, R>(S, s_b6, s_b7, s_b4, s_b5, a, s_blk, blk0, nblk_all, kvh, g0, k + 6, ng, n, cscale, active,
-                                wave, lane);
-    }
-  } else {
-    for (int k = 0; k < ng; k += 4) {
-      multi_pair<HD, BS, NW, R>(S, s_b0, s_b1, s_b2, s_b3, a, s_blk, blk0, nblk_all, kvh, g0, k, ng, n, cscale, active, wave,
-                                lane);
-      if (k + 2 >= ng) break;
-      multi_pair<HD, BS, NW, R>(S, s_b2, s_b3, s_b0, s_b1, a, s_blk, blk0, nblk_all, kvh, g0, k + 2, ng, n, cscale, active,
-                                wave, lane);
-    }
-  }
+  multi_run<HD, BS, NW>(S, s_b0, s_b1, s_b2, s_b3, s_b4, s_b5, s_b6, s_b7, a, s_blk, blk0, nblk_all, kvh, g0, ng, n,
+                        multi_cscale(a), active, wave, lane);
   const float lt = S.l + __shfl_xor(S.l, 32);
   if (!colv) return;
   const size_t vrow_head = ((size_t)r * Q + qi) * a.n_heads + kvh * G + hi;
@@ -2176,47 +2193,35 @@ decode_multi(DecodeArgs a) {
   }
 }
 
-// Combine the partitions of the multi-query read, 32 lanes per (row, query,
-// head): lane j reads partition j's (m, l); M = max m_j over partitions that
-// saw something, w_j = 2^(m_j - M) (0 for those that did not), L = sum l_j
-// w_j, and each lane sums w_j acc_j over its four hd values, the loads of
-// several partitions in flight at once.  out = O / L, or zeros when nothing
-// was visible.  kMultiMergeTuples tuples per 256-thread workgroup.
-constexpr int kMultiMergeTuples = 8;
-__global__ __launch_bounds__(256) void decode_multi_merge(DecodeArgs a) {
-  const int Q = a.query_len, HD = a.head_dim;
-  const int sub = threadIdx.x & 31;
-  const size_t vh = (size_t)blockIdx.x * kMultiMergeTuples + (threadIdx.x >> 5);  // (row * Q + query) * n_heads + head
-  if (vh >= (size_t)a.rows * Q * a.n_heads) return;  // a whole 32-lane half
-  const int r = (int)(vh / ((size_t)Q * a.n_heads));
-  const int cap = a.max_blocks_per_row * a.block_size;
-  int n = a.context_lens[r];
-  n = n < 0 ? 0 : (n > cap ? cap : n);
-  const int nparts = n > 0 ? (n + a.partition_tokens - 1) / a.partition_tokens : 1;
-  if (nparts <= 1) return;  // written directly by decode_multi
-  const WsLayout W = ws_layout(a.rows * Q, a.n_heads, a.max_parts, HD);
-  const size_t s0 = vh * a.max_parts;
-  float M = -INFINITY;  // the general path's maximum (more than four partitions)
+// Combine the partials of one (row, query, head) of the multi-query read,
+// 32 lanes: lane j reads partial j's (m, l) (m_at, l_at); M = max m_j over
+// partials that saw something, w_j = 2^(m_j - M) (0 for those that did
+// not), L = sum l_j w_j, and each lane sums w_j acc_j over its four hd
+// values (acc_at(j): partial j's hd row), the loads of several partials in
+// flight at once.  out = O / L, or zeros when nothing was visible.
+template <typename MAt, typename LAt, typename AccAt>
+__device__ __forceinline__ void merge_tuple(const DecodeArgs &a, int nparts, int sub, size_t out_base, MAt m_at,
+                                            LAt l_at, AccAt acc_at) {
+  const int HD = a.head_dim;
+  float M = -INFINITY;  // the general path's maximum (more than four partials)
   for (int j0 = 0; j0 < nparts && nparts > 4; j0 += 32)
-    if (j0 + sub < nparts) M = fmaxf(M, a.ws[W.m_off + s0 + j0 + sub]);
+    if (j0 + sub < nparts) M = fmaxf(M, m_at(j0 + sub));
 #pragma unroll
   for (int x = 16; x >= 1; x >>= 1) M = fmaxf(M, __shfl_xor(M, x, 32));
   const int d = 4 * sub;  // this lane's hd values d .. d + 3
   float L = 0.f;
   f32x4_t O = {0.f, 0.f, 0.f, 0.f};
   if (nparts <= 4) {
-    // every load in one round trip: m and l of partition `sub`, and this
-    // lane's acc values of all partitions (none depends on the maximum);
+    // every load in one round trip: m and l of partial `sub`, and this
+    // lane's acc values of all partials (none depends on the maximum);
     // then the same arithmetic, in the same order, as the general loop
     const bool own = sub < nparts;
-    const float mj = own ? a.ws[W.m_off + s0 + sub] : -INFINITY;
-    const float lj = own ? a.ws[W.l_off + s0 + sub] : 0.f;
-    const float *acc = a.ws + W.acc_off + s0 * HD + d;
+    const float mj = own ? m_at(sub) : -INFINITY;
+    const float lj = own ? l_at(sub) : 0.f;
     f32x4_t x[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u)
-      x[u] = u < nparts && d < HD ? *reinterpret_cast<const f32x4_t *>(acc + (size_t)u * HD)
-                                  : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      x[u] = u < nparts && d < HD ? *reinterpret_cast<const f32x4_t *>(acc_at(u) + d) : f32x4_t{0.f, 0.f, 0.f, 0.f};
     float M = mj;
 #pragma unroll
     for (int x2 = 16; x2 >= 1; x2 >>= 1) M = fmaxf(M, __shfl_xor(M, x2, 32));
@@ -2232,23 +2237,22 @@ __global__ __launch_bounds__(256) void decode_multi_merge(DecodeArgs a) {
   for (int j0 = 0; j0 < nparts && nparts > 4; j0 += 32) {
     float w = 0.f;
     if (j0 + sub < nparts && M != -INFINITY) {
-      const float mj = a.ws[W.m_off + s0 + j0 + sub];
+      const float mj = m_at(j0 + sub);
       w = mj == -INFINITY ? 0.f : exp2_fast(mj - M);
-      L = fmaf(a.ws[W.l_off + s0 + j0 + sub], w, L);
+      L = fmaf(l_at(j0 + sub), w, L);
     }
     const int cnt = min(32, nparts - j0);
-    const float *acc = a.ws + W.acc_off + (s0 + j0) * HD + d;
     int t = 0;
-    for (; t + 4 <= cnt; t += 4) {  // four partitions' loads in flight
+    for (; t + 4 <= cnt; t += 4) {  // four partials' loads in flight
       f32x4_t x[4];
 #pragma unroll
       for (int u = 0; u < 4; ++u)
-        x[u] = d < HD ? *reinterpret_cast<const f32x4_t *>(acc + (size_t)(t + u) * HD) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+        x[u] = d < HD ? *reinterpret_cast<const f32x4_t *>(acc_at(j0 + t + u) + d) : f32x4_t{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int u = 0; u < 4; ++u) O += __shfl(w, t + u, 32) * x[u];
     }
     for (; t < cnt; ++t) {
-      const f32x4_t x = d < HD ? *reinterpret_cast<const f32x4_t *>(acc + (size_t)t * HD) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      const f32x4_t x = d < HD ? *reinterpret_cast<const f32x4_t *>(acc_at(j0 + t) + d) : f32x4_t{0.f, 0.f, 0.f, 0.f};
       O += __shfl(w, t, 32) * x;
     }
   }
@@ -2257,19 +2261,286 @@ __global__ __launch_bounds__(256) void decode_multi_merge(DecodeArgs a) {
   if (d < HD) {
     const float inv = L > 0.f ? 1.f / L : 0.f;
 #pragma unroll
-    for (int e = 0; e < 4; ++e) store_out(a.out, a.out_dtype, vh * HD + d + e, L > 0.f ? O[e] * inv : 0.f);
+    for (int e = 0; e < 4; ++e) store_out(a.out, a.out_dtype, out_base + d + e, L > 0.f ? O[e] * inv : 0.f);
   }
+}
+
+// Combine the partitions of the multi-query read (merge_tuple over the
+// partition workspace), kMultiMergeTuples (row, query, head) tuples per
+// 256-thread workgroup.
+constexpr int kMultiMergeTuples = 8;
+__global__ __launch_bounds__(256) void decode_multi_merge(DecodeArgs a) {
+  const int Q = a.query_len, HD = a.head_dim;
+  const int sub = threadIdx.x & 31;
+  const size_t vh = (size_t)blockIdx.x * kMultiMergeTuples + (threadIdx.x >> 5);  // (row * Q + query) * n_heads + head
+  if (vh >= (size_t)a.rows * Q * a.n_heads) return;  // a whole 32-lane half
+  const int r = (int)(vh / ((size_t)Q * a.n_heads));
+  const int cap = a.max_blocks_per_row * a.block_size;
+  int n = a.context_lens[r];
+  n = n < 0 ? 0 : (n > cap ? cap : n);
+  const int nparts = n > 0 ? (n + a.partition_tokens - 1) / a.partition_tokens : 1;
+  if (nparts <= 1) return;  // written directly by decode_multi
+  const WsLayout W = ws_layout(a.rows * Q, a.n_heads, a.max_parts, HD);
+  const size_t s0 = vh * a.max_parts;
+  merge_tuple(
+      a, nparts, sub, vh * HD, [&](int j) { return a.ws[W.m_off + s0 + j]; },
+      [&](int j) { return a.ws[W.l_off + s0 + j]; },
+      [&](int j) { return (const float *)(a.ws + W.acc_off + (s0 + j) * HD); });
+}
+
+// ---------------------------------------------------------------------------
+// Balanced multi-query read: one query block covers all the queries of a
+// (row, kv head) and the batch has at most kWindowRows rows.  The groups of
+// 32 positions of every (kv head, row), in that order -- the one-query
+// read's stream -- are cut into at most a.stream_waves equal slices, one per
+// persistent workgroup of NW waves, so that every workgroup does the same
+// work whatever the length mix.  A workgroup walks the segments of its slice
+// (runs of one (kv head, row)) through the ring of multi_run, restarting it
+// between segments.  A (kv head, row) whole inside the slice is written to
+// out; a piece of one cut by a slice boundary leaves its partial (m, l and
+// acc for every column) in its slot (stream_piece_slot), which
+// decode_multi_stream_merge combines.  A segment spans at most
+// kMultiMaxPartition positions (the size of the block-id table); a longer
+// run of one (kv head, row) is read in several and keeps its softmax state.
+// ---------------------------------------------------------------------------
+// Stream length of a (kv head, row) of n positions in the balanced multi-
+// query read: its groups, behind kMultiSegmentCost groups of no work.
+__device__ __forceinline__ int multi_stream_groups(int n) {
+  return n > 0 ? (n + kGroupPositions - 1) / kGroupPositions + kMultiSegmentCost : 0;
+}
+
+template <int HD, int BS, int NW>
+__global__ __launch_bounds__(NW * kWave) __attribute__((amdgpu_waves_per_eu(NW / 4 > 1 ? NW / 4 : 1, 2))) void
+decode_multi_stream(DecodeArgs a) {
+  constexpr int KS = HD / 16, DT = HD / 32, NSLOT = HD / 8;
+  constexpr int R = multi_ring(NW);
+  constexpr int STAGE = NSLOT * kWave;
+  constexpr int LOG2_BS = BS == 8 ? 3 : (BS == 16 ? 4 : 5);
+  constexpr int NT = NW * kWave;
+  constexpr int RPT = (kWindowRows + NT - 1) / NT;  // rows per thread in the plan
+  constexpr int kSegGroups = kMultiMaxPartition / kGroupPositions;
+  __shared__ uint4 s_b0[STAGE], s_b1[STAGE], s_b2[STAGE], s_b3[STAGE];
+  __shared__ uint4 s_b4[R > 4 ? STAGE : 1], s_b5[R > 4 ? STAGE : 1], s_b6[R > 4 ? STAGE : 1], s_b7[R > 4 ? STAGE : 1];
+  __shared__ int32_t s_blk[kMultiMaxPartition / 8];
+  __shared__ int32_t s_ctx[kWindowRows], s_gpre[kWindowRows + 1];
+  __shared__ int32_t s_sum[NW];
+  const int tid = threadIdx.x;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int lane = tid & (kWave - 1), lr = lane & 31, h = lane >> 5;
+  const int G = a.group, Q = a.query_len, QB = a.q_per_tile, C = a.cols;
+  const int rows = a.rows;
+  const int cap = a.max_blocks_per_row * a.block_size;
+
+  // Plan: clamped lengths and the exclusive prefix of groups per row.
+  {
+    int len[RPT], loc = 0;
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = tid * RPT + i;
+      int x = r < rows ? a.context_lens[r] : 0;
+      len[i] = x < 0 ? 0 : (x > cap ? cap : x);
+      loc += multi_stream_groups(len[i]);
+    }
+    const int incl = wave_inclusive_scan(loc, lane);
+    if (lane == kWave - 1) s_sum[wave] = incl;
+    __syncthreads();
+    int run = incl - loc;
+    for (int v = 0; v < wave; ++v) run += s_sum[v];
+#pragma unroll
+    for (int i = 0; i < RPT; ++i) {
+      const int r = tid * RPT + i;
+      if (r < rows) {
+        s_ctx[r] = len[i];
+        s_gpre[r] = run;
+      }
+      run += multi_stream_groups(len[i]);
+    }
+    if (tid == 0) {
+      int total = 0;
+      for (int v = 0; v < NW; ++v) total += s_sum[v];
+      s_gpre[rows] = total;
+    }
+    __syncthreads();
+  }
+  const int ngk = __builtin_amdgcn_readfirstlane(s_gpre[rows]);  // every LDS value below is uniform: kept scalar
+  const long long ng_all = (long long)a.n_kv_heads * ngk;
+  long long waves = ng_all / max(a.cg_min, 1);
+  waves = waves < 1 ? 1 : (waves > a.stream_waves ? a.stream_waves : waves);
+  const int w = blockIdx.x;
+  if (w < rows && s_ctx[w] == 0) {  // an empty row reads zeros (all its queries); no slice visits it
+    const size_t per_row = (size_t)Q * a.n_heads * HD;
+    for (size_t idx = tid; idx < per_row; idx += NT) store_out(a.out, a.out_dtype, (size_t)w * per_row + idx, 0.f);
+  }
+  if (ng_all == 0 || w >= waves) return;  // the whole workgroup
+  const long long s1 = slice_start(w + 1, ng_all, waves);
+
+  // this lane's column: query q0 + lr / G, head kvh * G + lr % G of tile `wave`
+  const int q0 = wave * QB;
+  const int qi = q0 + lr / G, hi = lr % G;
+  const bool colv = lr < QB * G && qi < Q;
+  const bool active = q0 < Q;  // some column of this wave is a query
+  const uint32_t qsign = a.scale < 0.f ? 0x80008000u : 0u;  // fold a negative scale into q (exact)
+  const float cscale = multi_cscale(a);
+  const StreamLayout L = stream_layout(rows, C, HD, a.stream_waves);
+  MultiState<HD> S;
+  int cur_kvh = -1, cur_r = -1, pair_j0 = 0;
+  for (long long s = slice_start(w, ng_all, waves); s < s1;) {
+    const int kvh = (int)(s / ngk);
+    const int rem = (int)(s - (long long)kvh * ngk);
+    int lo = 0, hr = rows - 1;  // the row holding group `rem`: the last r with s_gpre[r] <= rem
+    while (lo < hr) {
+      const int mid = (lo + hr + 1) >> 1;
+      if (__builtin_amdgcn_readfirstlane(s_gpre[mid]) <= rem) lo = mid;
+      else hr = mid - 1;
+    }
+    const int r = lo;
+    const int jx = rem - __builtin_amdgcn_readfirstlane(s_gpre[r]);  // kMultiSegmentCost groups of no work, then the row's own
+    s += min((long long)max(kMultiSegmentCost - jx, 0), s1 - s);  // skip what is left of those
+    if (s == s1) break;
+    const int j0 = max(jx - kMultiSegmentCost, 0);
+    const int n = __builtin_amdgcn_readfirstlane(s_ctx[r]);
+    const int ngp = (n + kGroupPositions - 1) / kGroupPositions;
+    const int j1 = (int)min(min((long long)ngp, j0 + (s1 - s)), (long long)(j0 + kSegGroups));
+    __syncthreads();  // every wave is done with the previous segment's ring buffers and block ids
+    if (kvh != cur_kvh || r != cur_r) {  // a new (kv head, row): its queries and a fresh softmax state
+      pair_j0 = j0;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8_t x =
+            colv ? ld_bf16x8(a.q, ((((size_t)r * Q + qi) * a.n_heads + kvh * G + hi) * HD + 16 * ks + 8 * h) * 2)
+                 : zero_bf16x8();
+        uint4 u = __builtin_bit_cast(uint4, x);
+        u.x ^= qsign;
+        u.y ^= qsign;
+        u.z ^= qsign;
+        u.w ^= qsign;
+        S.qb[ks] = __builtin_bit_cast(bf16x8_t, u);
+      }
+      S.col_end = colv ? max(n - Q + qi + 1, 0) : INT_MAX;
+      S.min_end = active ? max(n - Q + q0 + 1, 0) : INT_MAX;
+      S.m = -INFINITY;
+      S.l = 0.f;
+#pragma unroll
+      for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+        for (int j = 0; j < 16; ++j) S.acc[dt][j] = 0.f;
+    }
+    // the segment's block ids, clamped into the pool
+    const int pos0 = j0 * kGroupPositions;
+    const int blk0 = pos0 >> LOG2_BS;
+    const int nblk = (min(j1 * kGroupPositions, n) - pos0 + BS - 1) >> LOG2_BS;
+    const int32_t *trow = a.block_table + (size_t)r * a.max_blocks_per_row + blk0;
+    for (int i = tid; i < nblk; i += NT) {
+      const int64_t b = trow[i];
+      s_blk[i] = (int32_t)(b < 0 ? 0 : (b >= a.num_blocks ? a.num_blocks - 1 : b));
+    }
+    __syncthreads();
+    multi_run<HD, BS, NW>(S, s_b0, s_b1, s_b2, s_b3, s_b4, s_b5, s_b6, s_b7, a, s_blk, blk0, nblk, kvh, j0, j1 - j0, n,
+                          cscale, active, wave, lane);
+    s += j1 - j0;
+    if (j1 == ngp || s == s1) {  // the (kv head, row) ends here, or the slice does
+      const float lt = S.l + __shfl_xor(S.l, 32);
+      if (colv) {
+        if (pair_j0 == 0 && j1 == ngp) {  // whole inside this slice
+          const size_t orow = (((size_t)r * Q + qi) * a.n_heads + kvh * G + hi) * HD;
+          const float inv = lt > 0.f ? 1.f / lt : 0.f;  // a query before the history reads zeros
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int j = 0; j < 16; ++j)
+              store_out(a.out, a.out_dtype, orow + 32 * dt + 8 * (j >> 2) + 4 * h + (j & 3), S.acc[dt][j] * inv);
+        } else {  // a piece: 2w + 1 if it starts the (kv head, row), else 2w
+          float *slot = a.ws + L.partials + (size_t)(pair_j0 == 0 ? 2 * w + 1 : 2 * w) * L.slot_stride;
+          // the stream column (query qi, head hi), formed here rather than held
+          // in a register across the loop
+          int cx = (int)threadIdx.x & 31;
+          asm volatile("" : "+v"(cx));
+          cx += q0 * G;
+          float *accp = slot + (size_t)cx * HD;
+#pragma unroll
+          for (int dt = 0; dt < DT; ++dt)
+#pragma unroll
+            for (int q4 = 0; q4 < 4; ++q4)
+              *reinterpret_cast<f32x4_t *>(accp + 32 * dt + 8 * q4 + 4 * h) =
+                  f32x4_t{S.acc[dt][4 * q4], S.acc[dt][4 * q4 + 1], S.acc[dt][4 * q4 + 2], S.acc[dt][4 * q4 + 3]};
+          if (h == 0) {
+            slot[(size_t)C * HD + cx] = S.m;
+            slot[(size_t)C * HD + C + cx] = lt;
+          }
+        }
+      }
+      cur_kvh = -1;
+    } else {
+      cur_kvh = kvh;
+      cur_r = r;
+    }
+  }
+}
+
+// Combine the pieces of the (kv head, row)s that the balanced multi-query
+// read cut, 32 lanes per (row, query, head) as in decode_multi_merge: the
+// same plan as the read finds the pieces (slots stream_piece_slot(first, k)).
+__global__ __launch_bounds__(256) void decode_multi_stream_merge(DecodeArgs a) {
+  __shared__ int32_t s_gpre[kWindowRows + 1];
+  __shared__ int32_t s_sum[256 / kWave];
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+  const int rows = a.rows, Q = a.query_len, HD = a.head_dim, C = a.cols, G = a.group;
+  const int cap = a.max_blocks_per_row * a.block_size;
+  {
+    int x = tid < rows ? a.context_lens[tid] : 0;
+    x = x < 0 ? 0 : (x > cap ? cap : x);
+    const int ng = multi_stream_groups(x);
+    const int incl = wave_inclusive_scan(ng, lane);
+    if (lane == kWave - 1) s_sum[wv] = incl;
+    __syncthreads();
+    int run = incl - ng;
+    for (int v = 0; v < wv; ++v) run += s_sum[v];
+    if (tid < rows) s_gpre[tid] = run;
+    if (tid == 0) s_gpre[rows] = s_sum[0] + s_sum[1] + s_sum[2] + s_sum[3];
+    __syncthreads();
+  }
+  const int sub = tid & 31;
+  const size_t vh = (size_t)blockIdx.x * kMultiMergeTuples + (tid >> 5);  // (row * Q + query) * n_heads + head
+  if (vh >= (size_t)rows * Q * a.n_heads) return;  // a whole 32-lane half
+  const int r = (int)(vh / ((size_t)Q * a.n_heads));
+  const int rem = (int)(vh - (size_t)r * Q * a.n_heads);
+  const int query = rem / a.n_heads, head = rem - query * a.n_heads;
+  const int kvh = head / G;
+  const int ngk = s_gpre[rows], g0 = s_gpre[r], ng = s_gpre[r + 1] - g0 - kMultiSegmentCost;
+  if (ng <= 0) return;  // zeros, written by the read
+  const long long ng_all = (long long)a.n_kv_heads * ngk;
+  long long waves = ng_all / max(a.cg_min, 1);
+  waves = waves < 1 ? 1 : (waves > a.stream_waves ? a.stream_waves : waves);
+  const long long Sg = (long long)kvh * ngk + g0 + kMultiSegmentCost;  // the row's first group of work
+  const long long first = slice_of(Sg, ng_all, waves);
+  const int nparts = (int)(slice_of(Sg + ng - 1, ng_all, waves) - first + 1);
+  if (nparts <= 1) return;  // written by the read
+  const StreamLayout L = stream_layout(rows, C, HD, a.stream_waves);
+  const int c = query * G + (head - kvh * G);
+  const float *parts = a.ws + L.partials;
+  merge_tuple(
+      a, nparts, sub, vh * HD,
+      [&](int j) { return parts[stream_piece_slot(first, j) * L.slot_stride + (size_t)C * HD + c]; },
+      [&](int j) { return parts[stream_piece_slot(first, j) * L.slot_stride + (size_t)C * HD + C + c]; },
+      [&](int j) { return parts + stream_piece_slot(first, j) * L.slot_stride + (size_t)c * HD; });
 }
 
 template <int HD, int BS, int NW>
 hipError_t launch_multi_t(const DecodeArgs &a, hipStream_t stream) {
+  const size_t tuples = (size_t)a.rows * a.query_len * a.n_heads;
+  const dim3 merge_grid((unsigned)((tuples + kMultiMergeTuples - 1) / kMultiMergeTuples));
+  if (a.stream == 2) {
+    hipLaunchKernelGGL((decode_multi_stream<HD, BS, NW>), dim3((unsigned)a.stream_waves), dim3(NW * kWave), 0, stream, a);
+    hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
+    hipLaunchKernelGGL(decode_multi_stream_merge, merge_grid, dim3(256), 0, stream, a);
+    return hipGetLastError();
+  }
   const long long units = (long long)a.max_parts * a.q_blocks * a.rows * a.n_kv_heads;
   hipLaunchKernelGGL((decode_multi<HD, BS, NW>), dim3((unsigned)units), dim3(NW * kWave), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
-  const size_t tuples = (size_t)a.rows * a.query_len * a.n_heads;
-  hipLaunchKernelGGL(decode_multi_merge, dim3((unsigned)((tuples + kMultiMergeTuples - 1) / kMultiMergeTuples)),
-                     dim3(256), 0, stream, a);
+  hipLaunchKernelGGL(decode_multi_merge, merge_grid, dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 

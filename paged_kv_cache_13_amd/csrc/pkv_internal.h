@@ -19,8 +19,10 @@ struct DecodeArgs {
   float *ws;  // workspace: partition layout (ws_layout) or stream layout (stream_layout)
   int32_t rows, n_heads, n_kv_heads, group, head_dim, block_size, log2_bs;
   int32_t max_blocks_per_row, partition_tokens, max_parts;
-  int32_t stream;  // 1: balanced stream decomposition (bf16, head_dim 64/128)
-  int32_t cg_min;  // stream path: minimum 32-position groups per wave
+  int32_t stream;  // 1: balanced stream decomposition (bf16, head_dim 64/128); 2: the
+                   // multi-query read's balanced decomposition (decode_multi_stream)
+  int32_t cg_min;  // stream paths: minimum 32-position groups per slice
+  int32_t stream_waves;  // stream paths: slices at most (persistent waves or workgroups)
   int32_t inplan;  // stream path: rows <= kWindowRows, each wave plans for itself
   int64_t num_blocks;
   int32_t dtype, out_dtype;
@@ -49,6 +51,15 @@ __host__ __device__ inline int32_t multi_waves(int32_t tiles) { return tiles > 4
 __host__ __device__ constexpr int multi_ring(int waves) { return waves >= 8 ? 8 : 4; }
 constexpr int kMultiMaxPartition = 4096;   // positions per multi-query partition, at most
 constexpr int32_t kMaxPartitionBlocks = 4096;  // block ids of one partition of the partition kernels, at most
+// Balanced multi-query read: each (kv head, row) enters the stream with this
+// many extra groups of no work ahead of its own, which charge a slice for
+// what every (kv head, row) it starts costs beyond its groups (the restart:
+// block ids, queries, the ring's first groups; and the output or partial
+// written at its end), so that slices balance time, not groups.  Measured
+// on the 8B shape (us per call, 0 / 4 / 8 / 12 / 16 / 24 / 32 groups):
+// 16 rows x 64 queries 109.6 / 103.0 / 98.9 / 90.3 / 90.0 / 92.4 / 96.1,
+// 64 x 64 316.7 / 297.7 / 281.3 / 265.9 / 264.3 / 266.6 / 271.7.
+constexpr int kMultiSegmentCost = 12;
 
 // Workspace of the split-context read, in floats: running max m and sum l
 // per (row, query head, partition), then the fp32 partial output rows.
@@ -67,12 +78,14 @@ __host__ __device__ inline WsLayout ws_layout(int32_t rows, int32_t n_heads, int
 }
 
 // Stream decomposition of the bf16 read: the groups of 32 positions of all
-// (kv head, row) pairs, in that order, are cut into kStreamWaves equal
-// contiguous slices, one per persistent wave.  Workspace, in 4-byte words:
+// (kv head, row) pairs, in that order, are cut into equal contiguous slices,
+// one per persistent wave (at most kStreamWaves of them; the multi-query
+// read's balanced form cuts at most one slice per persistent workgroup).
+// Workspace, in 4-byte words, for at most `waves` slices:
 //   hdr[4]                 groups per kv head, waves used, two words unused
 //   first_pos[2 * waves]   (kv head * rows + row, group) where each wave starts
 //   gpre[rows + 1]         exclusive prefix of groups per row
-//   partials[2 * kStreamWaves][slot]  fp32 acc[cols][hd], m[cols], l[cols]
+//   partials[2 * waves][slot]  fp32 acc[cols][hd], m[cols], l[cols]
 // The plan words (hdr, first_pos, gpre) are written by decode_plan; a batch
 // of at most kWindowRows rows is planned inside every wave and leaves them
 // unused.
@@ -95,14 +108,15 @@ struct StreamLayout {
   size_t slot_stride;
 };
 __host__ __device__ inline size_t align4(size_t x) { return (x + 3) & ~(size_t)3; }
-__host__ __device__ inline StreamLayout stream_layout(int32_t rows, int32_t cols, int32_t head_dim) {
+__host__ __device__ inline StreamLayout stream_layout(int32_t rows, int32_t cols, int32_t head_dim,
+                                                      int32_t waves = kStreamWaves) {
   StreamLayout L;
   L.hdr = 0;
   L.first_pos = 4;
-  L.gpre = L.first_pos + 2 * (size_t)kStreamWaves;
+  L.gpre = L.first_pos + 2 * (size_t)waves;
   L.partials = align4(L.gpre + (size_t)rows + 1);
   L.slot_stride = align4((size_t)cols * (head_dim + 2));
-  L.total = L.partials + 2 * (size_t)kStreamWaves * L.slot_stride;
+  L.total = L.partials + 2 * (size_t)waves * L.slot_stride;
   return L;
 }
 // Slot of piece k of a cut pair whose first piece lies in slice `first`.

@@ -362,20 +362,34 @@ def test_multi_query_workspace(lib):
     head = 4 + 2 * 1024 + 65
     head = (head + 3) & ~3
     assert ws(d, 4) == (head + 2 * 1024 * 16 * 130) * 4
-    # 8 queries (32 columns): the workgroup path.  64 rows x 8 kv heads x one
-    # query block (a two-wave workgroup, two per compute unit) = 512 blocks
-    # on 512 slots: a 4096-position table wants 4096-position partitions,
-    # capped at 1024 for two-wave workgroups, so it splits in 4: m, l and a
-    # 128-float acc per (row, query, head, partition)
-    slots = 64 * 8 * 32 * 4
-    assert ws(d, 8) == (((2 * slots + 3) & ~3) + slots * 128) * 4
-    # 16 rows: 128 blocks want 1024-position partitions (4 of them)
-    slots16 = 16 * 8 * 32 * 4
-    assert ws(desc(rows=16), 8) == (((2 * slots16 + 3) & ~3) + slots16 * 128) * 4
+    # 8 queries (32 columns), one query block per (row, kv head), <= 256
+    # rows: the balanced multi-query read.  One 2-wave workgroup per slice,
+    # two per compute unit (512); the stream layout for 512 slices: header,
+    # slice starts, row prefixes, then two slots per slice of 32 x (128 + 2)
+    # floats.  A caller's partition sets the slice minimum only.
+    def balanced(rows, cols, slices):
+        head = (4 + 2 * slices + rows + 1 + 3) & ~3
+        return (head + 2 * slices * ((cols * 130 + 3) & ~3)) * 4
+    assert ws(d, 8) == balanced(64, 32, 512)
+    assert ws(desc(rows=16), 8) == balanced(16, 32, 512)
+    assert ws(desc(partition_tokens=1008), 8) == balanced(64, 32, 512)
+    # 64 queries (256 columns, 8 waves, one workgroup per compute unit)
+    assert ws(desc(rows=16), 64) == balanced(16, 256, 256)
+    # the workgroup path: two query blocks (100 queries of 4 heads: 13
+    # tiles of 32 columns, blocks of 8 waves), or more than 256 rows.
+    # 64 rows x 8 kv heads x 2 blocks = 1024 workgroups on 256 slots: a
+    # 4096-position table wants 16384-position partitions, capped at 2048
+    # for 8-wave workgroups: 2 partitions of m, l and a 128-float acc per
+    # (row, query, head, partition)
+    def parts(rows, q, p):
+        slots = rows * q * 32 * p
+        return (((2 * slots + 3) & ~3) + slots * 128) * 4
+    assert ws(d, 100) == parts(64, 100, 2)
+    # 300 rows, 8 queries: 2-wave workgroups stop at 1024 positions (4 parts)
+    assert ws(desc(rows=300), 8) == parts(300, 8, 4)
     # a caller's partition (a multiple of the block size) is rounded up to
     # 32 positions and capped at 4096
-    slots4 = 64 * 8 * 32 * 4
-    assert ws(desc(partition_tokens=1008), 8) == (((2 * slots4 + 3) & ~3) + slots4 * 128) * 4
-    assert ws(desc(partition_tokens=8192), 8) == 0   # capped at 4096: one partition, written directly
-    assert ws(desc(max_blocks_per_row=64, partition_tokens=1024), 8) == 0
+    assert ws(desc(partition_tokens=1008), 100) == parts(64, 100, 4)
+    assert ws(desc(partition_tokens=8192), 100) == 0   # capped at 4096: one partition, written directly
+    assert ws(desc(max_blocks_per_row=64, partition_tokens=1024), 100) == 0
     assert ws(desc(dtype=0, out_dtype=0), 4) == 0    # refused descriptors need nothing

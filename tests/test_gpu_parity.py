@@ -617,6 +617,55 @@ def test_multi_query_stream_path_matches_oracle(H, KV, hd, bs, lo, hi, qlen, par
     check_multi(b, q, part)
 
 
+# At least 128 (row, kv head) pairs, one query block per pair: the balanced
+# multi-query read (slices of the (kv head, row) group stream, one per
+# persistent workgroup; partition_tokens sets the slice minimum).  Workgroups
+# of 8, 4 and 2 waves; head_dim 64 and 128; blocks of 8, 16 and 32; slices
+# of one and two groups (pieces everywhere); rows shorter than the chunk;
+# long rows in slices of 256 groups (read in 128-group segments); G = 3
+# (30 of a tile's 32 columns); G = 8 with one kv head.
+@pytest.mark.parametrize("rows,H,KV,hd,bs,lo,hi,qlen,part", [
+    (16, 32, 8, 128, 16, 1, 900, 64, 0), (16, 32, 8, 128, 8, 100, 1500, 24, 64),
+    (32, 16, 4, 64, 32, 1, 700, 10, 32), (128, 8, 1, 128, 16, 50, 600, 3, 0),
+    (16, 24, 8, 128, 16, 3000, 9000, 6, 8192), (16, 32, 8, 64, 8, 1, 300, 40, 0),
+])
+def test_multi_query_balanced_matches_oracle(rows, H, KV, hd, bs, lo, hi, qlen, part):
+    note("multi balanced rows=%d H=%d KV=%d hd=%d bs=%d q=%d part=%d" % (rows, H, KV, hd, bs, qlen, part))
+    b, q = multi_case(rows, H, KV, hd, bs, lo, hi, qlen, seed=rows + hd + bs + qlen)
+    check_multi(b, q, part)
+
+
+def test_multi_query_balanced_ignores_poisoned_slots_bitwise():
+    cfg = synth.DecodeConfig("multi", "bf16", rows=16, n_heads=32, n_kv_heads=8, head_dim=128, block_size=16,
+                             ctx=("uniform", 1, 900), pool=("factor", 1.5), max_ctx=900, seed=63)
+    clean = synth.make_batch(cfg, device=DEV, poison=False)
+    dirty = synth.make_batch(cfg, device=DEV, poison=True)
+    assert torch.isnan(dirty.k_pool.float()).any() and torch.isnan(dirty.v_pool.float()).any()
+    g = torch.Generator(device=DEV).manual_seed(64)
+    q = torch.randn(16, 20, 32, 128, generator=g, device=DEV).to(torch.bfloat16)
+    outs = []
+    for b in (clean, dirty):
+        outs.append(pkv.paged_attention_multi(q, b.k_pool, b.v_pool, b.block_table, b.context_lens, b.scale,
+                                              out=torch.empty(q.shape, dtype=torch.float32, device=DEV),
+                                              partition_tokens=64))
+    torch.cuda.synchronize()
+    assert torch.isfinite(outs[1]).all()
+    assert torch.equal(outs[0], outs[1])
+
+
+def test_multi_query_balanced_rows_shorter_than_the_chunk_read_zeros():
+    b, q = multi_case(16, 32, 8, 128, 16, 1, 30, 32, seed=65)
+    b.context_lens[3] = 0  # an empty row reads zeros for every query
+    b.ctx_host[3] = 0
+    got = pkv.paged_attention_multi(q, b.k_pool, b.v_pool, b.block_table, b.context_lens, b.scale)
+    torch.cuda.synchronize()
+    ref = multi_oracle(b, q)
+    assert_close(got.float().cpu(), ref, what="short rows", **TOL[torch.bfloat16])
+    for r in range(16):
+        n = int(b.ctx_host[r])
+        assert (got[r, :32 - n].float() == 0).all()
+
+
 def check_multi(b, q, part):
     got = pkv.paged_attention_multi(q, b.k_pool, b.v_pool, b.block_table, b.context_lens, b.scale,
                                     partition_tokens=part)
