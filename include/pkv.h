@@ -226,14 +226,26 @@ int pkv_paged_attention_noalloc(const pkv_attn_desc *d, const void *q, const voi
  * significant bits (a bf16 hi + lo pair).
  *
  *   d             as for pkv_paged_attention; dtype must be PKV_BF16 and
- *                 head_dim 64 or 128 (else PKV_ERR_DTYPE / PKV_ERR_HEAD_DIM);
- *                 partition_tokens is rounded up to a multiple of 32 and
- *                 capped at 4096 (0: chosen from the shapes).  A chunk with
- *                 query_len * (n_heads / n_kv_heads) <= 16 over a table of
- *                 at least 32 * 1024 groups of 32 positions (rows x kv heads
- *                 x table width) runs on pkv_paged_attention's stream
- *                 decomposition instead, where partition_tokens is the
- *                 minimum slice length as there.
+ *                 head_dim 64 or 128 (else PKV_ERR_DTYPE / PKV_ERR_HEAD_DIM).
+ *                 The read takes one of three decompositions (host shapes
+ *                 only), and partition_tokens means:
+ *                 - query_len * (n_heads / n_kv_heads) <= 16 over a table of
+ *                   at least 32 * 1024 groups of 32 positions (rows x kv
+ *                   heads x table width): pkv_paged_attention's stream
+ *                   decomposition; partition_tokens is the minimum slice
+ *                   length as there;
+ *                 - else, when one workgroup holds all of a row's queries
+ *                   (query_len * group <= 256 columns of 32-column tiles, at
+ *                   most 8 tiles), rows <= 256 and rows x kv heads >= 128:
+ *                   the balanced read, equal slices of the (kv head, row)
+ *                   stream of 32-position groups, one per persistent
+ *                   workgroup (every (kv head, row) also charged 12 groups
+ *                   for its start); partition_tokens, rounded up to whole
+ *                   groups, is the minimum slice (0: 16 groups);
+ *                 - else partitions of whole 32-position groups, one
+ *                   workgroup per (partition, query block, kv head, row);
+ *                   partition_tokens is rounded up to a multiple of 32 and
+ *                   capped at 4096 (0: chosen from the shapes).
  *   query_len     1 .. 65535
  *   q, out        device [rows, query_len, n_heads, head_dim]
  *   workspace     >= pkv_paged_attention_multi_workspace_size(d, query_len)
