@@ -210,11 +210,13 @@ static int gathered_read(int32_t rows, int32_t n_heads, int32_t n_kv_heads,
   return ORC_OK;
 }
 
-/* The gathered read in the pages' own interface: a whole-history slot mapping
- * [rows, width] (Day 25 page: the cache hands the read its pools and the slot
- * mapping for the whole history).  *score_cells receives the size of the
- * score rectangle this read materialises, rows * n_heads * 1 * width (the
- * Day 60 page's rectangle; query length is 1 in decode). */
+/* The gathered read, driven by slots instead of a block table: row r's
+ * position t lives at pool slot slot_mapping[r * width + t] ("Day 25: the
+ * fused read dispatches to the kernel backend", "What I added today").
+ * *score_cells receives the number of scores this read holds at once,
+ * rows * n_heads * 1 * width ("Day 60: the read becomes a choice, and a
+ * counter is what can see it", "What I added today"; one query per row in
+ * decode). */
 int oracle_paged_attention_slots(int32_t rows, int32_t n_heads,
                                  int32_t n_kv_heads, int32_t head_dim,
                                  int32_t block_size, int64_t num_blocks,
