@@ -617,8 +617,8 @@ int32_t pkv_read_tile(const pkv_attn_desc *d) {
   Plan pl;
   if (plan_decode(d, &pl) != PKV_OK) return 0;
   if (pl.stream) return pkv::kGroupPositions;  // one wave, one group
-  if (d->dtype == PKV_BF16 && (d->head_dim == 64 || d->head_dim == 128))
-    return 4 * pkv::kGroupPositions;  // decode_partition_mfma: four waves, one group each
+  if (d->dtype == PKV_BF16 && (d->head_dim == 64 || d->head_dim == 128))  // decode_partition_mfma: a group per wave
+    return pkv::mfma_partition_waves(pl.max_parts, d->n_kv_heads, d->rows) * pkv::kGroupPositions;
   // decode_partition: four waves x four 16-byte loads per lane, each load
   // covering 64 / (head_dim / (16 / elem)) positions
   return (int32_t)(1024 * (16 / elem_bytes(d->dtype)) / d->head_dim);

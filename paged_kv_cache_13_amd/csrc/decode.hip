@@ -829,8 +829,10 @@ __device__ __forceinline__ void token_store(const TokenRow<HD> &t, const DecodeA
   }
 }
 
-template <int HD, int BS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void decode_partition_mfma(DecodeArgs a) {
+template <int HD, int BS, int NWV>
+__global__ __launch_bounds__(NWV * kWave) __attribute__((amdgpu_waves_per_eu(2))) void decode_partition_mfma(DecodeArgs a) {
+  constexpr int kWaves = NWV;  // four, or eight for a grid of at most one workgroup per compute unit
+  constexpr int kThreads = NWV * kWave;
   constexpr int KS = HD / 32, DT = HD / 16, GT = 32;
   __shared__ float s_m[kWaves][16];
   __shared__ float s_l[kWaves][16];
@@ -975,7 +977,10 @@ template <int HD, int BS>
 hipError_t launch_mfma(const DecodeArgs &a, hipStream_t stream) {
   const dim3 grid((unsigned)a.max_parts * a.n_kv_heads * a.rows);
   const size_t lds = (size_t)(a.partition_tokens >> a.log2_bs) * sizeof(int32_t);
-  hipLaunchKernelGGL((decode_partition_mfma<HD, BS>), grid, dim3(kThreads), lds, stream, a);
+  if (mfma_partition_waves(a.max_parts, a.n_kv_heads, a.rows) == 8)
+    hipLaunchKernelGGL((decode_partition_mfma<HD, BS, 8>), grid, dim3(8 * kWave), lds, stream, a);
+  else
+    hipLaunchKernelGGL((decode_partition_mfma<HD, BS, 4>), grid, dim3(kThreads), lds, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
   hipLaunchKernelGGL(decode_merge, dim3((unsigned)a.rows * a.n_heads), dim3(128), 0, stream, a);

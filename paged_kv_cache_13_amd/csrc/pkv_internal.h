@@ -60,6 +60,12 @@ constexpr int32_t kMaxPartitionBlocks = 4096;  // block ids of one partition of 
 // 16 rows x 64 queries 109.6 / 103.0 / 98.9 / 90.3 / 90.0 / 92.4 / 96.1,
 // 64 x 64 316.7 / 297.7 / 281.3 / 265.9 / 264.3 / 266.6 / 271.7.
 constexpr int kMultiSegmentCost = 12;
+// Waves per workgroup of the matrix-core partition read: eight (two per
+// SIMD) when the grid is at most one workgroup per compute unit, so that a
+// short read has two waves per SIMD to hide its load latency; else four.
+__host__ __device__ inline int mfma_partition_waves(int32_t max_parts, int32_t n_kv_heads, int32_t rows) {
+  return (long long)max_parts * n_kv_heads * rows <= 256 ? 8 : 4;
+}
 
 // Workspace of the split-context read, in floats: running max m and sum l
 // per (row, query head, partition), then the fp32 partial output rows.

@@ -300,7 +300,8 @@ def test_read_counters_window_and_refusals(lib):
 def test_read_tile_names_what_each_read_holds(lib):
     tile = lambda **kw: lib.pkv_read_tile(ctypes.byref(desc(**kw)))
     assert tile() == 32                                   # stream read: one wave, one group
-    assert tile(rows=8, max_blocks_per_row=64) == 128     # matrix-core partition read
+    assert tile(rows=8, max_blocks_per_row=64) == 256     # matrix-core partition read, 8 waves (128 workgroups)
+    assert tile(rows=64, max_blocks_per_row=64) == 128    # 4 waves: 512 workgroups
     assert tile(dtype=0, out_dtype=0, head_dim=64) == 64  # VALU partition read, fp32
     assert tile(dtype=0, out_dtype=0, head_dim=128) == 32
     assert tile(dtype=0, out_dtype=0, head_dim=16) == 256
