@@ -2039,6 +2039,30 @@ __device__ __forceinline__ void multi_pair(MultiState<HD> &S, const uint4 *c0, c
   }
 }
 
+// A column's output row (hd values at `orow`), from its accumulators scaled
+// by inv: register j of acc[dt] is hd 32 dt + 8 (j / 4) + 4 h + j % 4, so
+// each quad of registers is four consecutive hd values, stored as one
+// 16-byte (fp32) or 8-byte (bf16, round to nearest even) store.
+template <int HD>
+__device__ __forceinline__ void multi_store_row(const DecodeArgs &a, size_t orow, const f32x16_t *acc, float inv,
+                                                int h) {
+#pragma unroll
+  for (int dt = 0; dt < HD / 32; ++dt)
+#pragma unroll
+    for (int q4 = 0; q4 < 4; ++q4) {
+      const size_t o = orow + 32 * dt + 8 * q4 + 4 * h;
+      const float x0 = acc[dt][4 * q4] * inv, x1 = acc[dt][4 * q4 + 1] * inv;
+      const float x2 = acc[dt][4 * q4 + 2] * inv, x3 = acc[dt][4 * q4 + 3] * inv;
+      if (a.out_dtype == kF32) {
+        *reinterpret_cast<f32x4_t *>(static_cast<float *>(a.out) + o) = f32x4_t{x0, x1, x2, x3};
+      } else {
+        const uint32_t w0 = f32_to_bf16_rne(x0) | ((uint32_t)f32_to_bf16_rne(x1) << 16);
+        const uint32_t w1 = f32_to_bf16_rne(x2) | ((uint32_t)f32_to_bf16_rne(x3) << 16);
+        *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + o) = make_uint2(w0, w1);
+      }
+    }
+}
+
 // c > 0 for the statistics; a zero scale becomes 1e-30 (every weight still
 // exp2(0) = 1) and a NaN scale stays NaN
 __device__ __forceinline__ float multi_cscale(const DecodeArgs &a) {
@@ -2175,12 +2199,7 @@ decode_multi(DecodeArgs a) {
   if (!colv) return;
   const size_t vrow_head = ((size_t)r * Q + qi) * a.n_heads + kvh * G + hi;
   if (nparts == 1) {
-    const float inv = lt > 0.f ? 1.f / lt : 0.f;  // a query before the history reads zeros
-#pragma unroll
-    for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-      for (int j = 0; j < 16; ++j)
-        store_out(a.out, a.out_dtype, vrow_head * HD + 32 * dt + 8 * (j >> 2) + 4 * h + (j & 3), S.acc[dt][j] * inv);
+    multi_store_row<HD>(a, vrow_head * HD, S.acc, lt > 0.f ? 1.f / lt : 0.f, h);  // 0: a query before the history
   } else {
     const WsLayout W = ws_layout(a.rows * Q, a.n_heads, a.max_parts, HD);
     const size_t slot = vrow_head * a.max_parts + part;
@@ -2448,12 +2467,7 @@ decode_multi_stream(DecodeArgs a) {
       if (colv) {
         if (pair_j0 == 0 && j1 == ngp) {  // whole inside this slice
           const size_t orow = (((size_t)r * Q + qi) * a.n_heads + kvh * G + hi) * HD;
-          const float inv = lt > 0.f ? 1.f / lt : 0.f;  // a query before the history reads zeros
-#pragma unroll
-          for (int dt = 0; dt < DT; ++dt)
-#pragma unroll
-            for (int j = 0; j < 16; ++j)
-              store_out(a.out, a.out_dtype, orow + 32 * dt + 8 * (j >> 2) + 4 * h + (j & 3), S.acc[dt][j] * inv);
+          multi_store_row<HD>(a, orow, S.acc, lt > 0.f ? 1.f / lt : 0.f, h);  // 0: a query before the history
         } else {  // a piece: 2w + 1 if it starts the (kv head, row), else 2w
           float *slot = a.ws + L.partials + (size_t)(pair_j0 == 0 ? 2 * w + 1 : 2 * w) * L.slot_stride;
           // the stream column (query qi, head hi), formed here rather than held
