@@ -2282,10 +2282,17 @@ __device__ __forceinline__ void merge_tuple(const DecodeArgs &a, int nparts, int
   }
 #pragma unroll
   for (int x = 16; x >= 1; x >>= 1) L += __shfl_xor(L, x, 32);
-  if (d < HD) {
+  if (d < HD) {  // four consecutive hd values: one 16-byte (fp32) or 8-byte (bf16) store
     const float inv = L > 0.f ? 1.f / L : 0.f;
-#pragma unroll
-    for (int e = 0; e < 4; ++e) store_out(a.out, a.out_dtype, out_base + d + e, L > 0.f ? O[e] * inv : 0.f);
+    const float y0 = L > 0.f ? O[0] * inv : 0.f, y1 = L > 0.f ? O[1] * inv : 0.f;
+    const float y2 = L > 0.f ? O[2] * inv : 0.f, y3 = L > 0.f ? O[3] * inv : 0.f;
+    if (a.out_dtype == kF32) {
+      *reinterpret_cast<f32x4_t *>(static_cast<float *>(a.out) + out_base + d) = f32x4_t{y0, y1, y2, y3};
+    } else {
+      const uint32_t w0 = f32_to_bf16_rne(y0) | ((uint32_t)f32_to_bf16_rne(y1) << 16);
+      const uint32_t w1 = f32_to_bf16_rne(y2) | ((uint32_t)f32_to_bf16_rne(y3) << 16);
+      *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + out_base + d) = make_uint2(w0, w1);
+    }
   }
 }
 
