@@ -34,7 +34,7 @@ HBM_PEAK_GBS = 8000.0
 # (profiles/decode_stream_<workload>_hbm_counters.md), valid only for the
 # kernel sources they were taken on.
 PROFILED_TRAFFIC = {
-    "llama3_8b_layer": {"src": "11f842b21b3a774e", "step_bytes": 577256903, "read_bytes": 576615505},
+    "llama3_8b_layer": {"src": "3463aa13cb6eb425", "step_bytes": 577254397, "read_bytes": 576652625},
 }
 KERNEL_SOURCES = ("decode.hip", "pkv_internal.h", "abi.hip")
 
