@@ -1821,21 +1821,6 @@ __device__ __forceinline__ void stage_multi(uint4 *st, const DecodeArgs &a, cons
 }
 
 
-// Until at most `ahead` (0 .. R - 4) later groups of this wave's staging
-// loads (SPW each) are in flight, and every LDS read of this wave has
-// returned.  s_waitcnt takes an immediate: one case per count.
-template <int SPW, int R>
-__device__ __forceinline__ void wait_ring(int ahead) {
-  static_assert(R == 4 || R == 8, "ring of 4 or 8 groups");
-  if constexpr (R == 8) {
-    if (ahead >= 4) { __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(4 * SPW)); return; }
-    if (ahead == 3) { __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(3 * SPW)); return; }
-    if (ahead == 2) { __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(2 * SPW)); return; }
-    if (ahead == 1) { __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(SPW)); return; }
-  }
-  __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
-}
-
 // Per-wave state of the multi-query read: this lane's column and its
 // softmax state.  acc[dt] register j is output hd 32 dt + 8 (j / 4) +
 // 4 (lane / 32) + j % 4 of the column.
@@ -1918,24 +1903,26 @@ __device__ __forceinline__ void multi_v(bf16x8_t (&vc)[HD / 32][2], const uint4 
   }
 }
 
+template <int HD>
+__device__ __forceinline__ void multi_pair_compute(MultiState<HD> &S, const uint4 *c0, const uint4 *c1,
+                                                   const DecodeArgs &a, int g0, int k, int ng, int n, float cscale,
+                                                   int lane);
+
 // Groups k and k + 1 of the multi-query read (k even; k + 1 may lie past
-// the partition's last group), from a ring of R group buffers.  Wait for
-// both and publish them -- the barrier also says every wave is done with
-// groups k - 2 and k - 1, whose buffers are then refilled with groups
-// k + R - 2 and k + R - 1 -- then the scores
-// of both groups (two independent MFMA chains), one softmax update over
-// their 64 positions (one max exchange, one rescale check) and the P.V
-// products.  The ring's buffers are separate LDS arrays and each step names
-// its four statically, so the compiler can tell the reads of these groups
-// from the loads in flight into the others.
+// the partition's last group), from a ring of R = 4 group buffers.  Wait
+// for both and publish them -- the barrier also says every wave is done
+// with groups k - 2 and k - 1, whose buffers are then refilled with groups
+// k + 2 and k + 3 -- then compute them (multi_pair_compute).  The ring's
+// buffers are separate LDS arrays and each step names its four statically,
+// so the compiler can tell the reads of these groups from the loads in
+// flight into the others.
 template <int HD, int BS, int NW, int R>
 __device__ __forceinline__ void multi_pair(MultiState<HD> &S, const uint4 *c0, const uint4 *c1, uint4 *r0, uint4 *r1,
                                            const DecodeArgs &a, const int32_t *s_blk, int blk0, int nblk, int kvh, int g0,
                                            int k, int ng, int n, float cscale, bool active, int wave, int lane) {
-  constexpr int KS = HD / 16, DT = HD / 32, SPW = HD / 8 / NW;
-  // this wave's loads of groups k, k + 1 have landed; those of up to R - 4
-  // later groups may stay in flight
-  wait_ring<SPW, R>(min(ng - 2 - k, R - 4));
+  static_assert(R == 4, "the ring of eight steps by four groups (multi_quad)");
+  // this wave's loads (groups k and k + 1: the ring holds no others) have landed
+  __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
@@ -1944,6 +1931,44 @@ __device__ __forceinline__ void multi_pair(MultiState<HD> &S, const uint4 *c0, c
   if (k + R - 1 < ng)
     stage_multi<HD, BS, NW>(r1, a, s_blk, blk0, nblk, kvh, (g0 + k + R - 1) * kGroupPositions, n - 1, wave, lane);
   if (!active) return;
+  multi_pair_compute<HD>(S, c0, c1, a, g0, k, ng, n, cscale, lane);
+}
+
+// Eight groups k .. k + 7 pass through a ring of R = 8 buffers four at a
+// time: wait for all of this wave's loads (groups k .. k + 3, staged one
+// step earlier) and publish them -- the barrier also says every wave is done
+// with groups k - 4 .. k - 1 -- refill those four buffers with groups
+// k + 4 .. k + 7, then compute groups k .. k + 3 as two pairs.  One wait and
+// one barrier per four groups, and a step of computation to hide each load.
+template <int HD, int BS, int NW>
+__device__ __forceinline__ void multi_quad(MultiState<HD> &S, const uint4 *c0, const uint4 *c1, const uint4 *c2,
+                                           const uint4 *c3, uint4 *r0, uint4 *r1, uint4 *r2, uint4 *r3,
+                                           const DecodeArgs &a, const int32_t *s_blk, int blk0, int nblk, int kvh,
+                                           int g0, int k, int ng, int n, float cscale, bool active, int wave,
+                                           int lane) {
+  __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+  uint4 *const r[4] = {r0, r1, r2, r3};
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (k + 4 + i < ng)
+      stage_multi<HD, BS, NW>(r[i], a, s_blk, blk0, nblk, kvh, (g0 + k + 4 + i) * kGroupPositions, n - 1, wave, lane);
+  if (!active) return;
+  multi_pair_compute<HD>(S, c0, c1, a, g0, k, ng, n, cscale, lane);
+  if (k + 2 < ng) multi_pair_compute<HD>(S, c2, c3, a, g0, k + 2, ng, n, cscale, lane);
+}
+
+// Groups k and k + 1 from buffers c0 and c1, already published: the scores
+// of both groups (two independent MFMA chains), one softmax update over
+// their 64 positions (one max exchange, one rescale check) and the P.V
+// products.
+template <int HD>
+__device__ __forceinline__ void multi_pair_compute(MultiState<HD> &S, const uint4 *c0, const uint4 *c1,
+                                                   const DecodeArgs &a, int g0, int k, int ng, int n, float cscale,
+                                                   int lane) {
+  constexpr int KS = HD / 16, DT = HD / 32;
   const int h = lane >> 5;
   const bool two = k + 1 < ng;
   const int gb0 = (g0 + k) * kGroupPositions, gb1 = gb0 + kGroupPositions;
@@ -2071,10 +2096,11 @@ __device__ __forceinline__ float multi_cscale(const DecodeArgs &a) {
 }
 
 // Groups g0 .. g0 + ng - 1 of (row, kv head) through the ring: the prologue
-// stages the first R - 2, then the pairs (multi_pair).  s_blk holds the
-// block ids from block blk0 on (nblk of them) and has been published; on
-// return every staged load has been consumed, but other waves may still be
-// reading the ring's last buffers.
+// stages the first four (a ring of eight) or two (a ring of four), then the
+// steps (multi_quad or multi_pair).  s_blk holds the block ids from block
+// blk0 on (nblk of them) and has been published; on return every staged
+// load has been consumed, but other waves may still be reading the ring's
+// last buffers.
 template <int HD, int BS, int NW>
 __device__ __forceinline__ void multi_run(MultiState<HD> &S, uint4 *s_b0, uint4 *s_b1, uint4 *s_b2, uint4 *s_b3,
                                           uint4 *s_b4, uint4 *s_b5, uint4 *s_b6, uint4 *s_b7, const DecodeArgs &a,
@@ -2090,22 +2116,12 @@ __device__ __forceinline__ void multi_run(MultiState<HD> &S, uint4 *s_b0, uint4 
   if constexpr (R == 8) {
     stage(s_b2, 2);
     stage(s_b3, 3);
-    stage(s_b4, 4);
-    stage(s_b5, 5);
-  }
-  if constexpr (R == 8) {
     for (int k = 0; k < ng; k += 8) {
-      multi_pair<HD, BS, NW, R>(S, s_b0, s_b1, s_b6, s_b7, a, s_blk, blk0, nblk, kvh, g0, k, ng, n, cscale, active, wave,
-                                lane);
-      if (k + 2 >= ng) break;
-      multi_pair<HD, BS, NW, R>(S, s_b2, s_b3, s_b0, s_b1, a, s_blk, blk0, nblk, kvh, g0, k + 2, ng, n, cscale, active,
-                                wave, lane);
+      multi_quad<HD, BS, NW>(S, s_b0, s_b1, s_b2, s_b3, s_b4, s_b5, s_b6, s_b7, a, s_blk, blk0, nblk, kvh, g0, k, ng,
+                             n, cscale, active, wave, lane);
       if (k + 4 >= ng) break;
-      multi_pair<HD, BS, NW, R>(S, s_b4, s_b5, s_b2, s_b3, a, s_blk, blk0, nblk, kvh, g0, k + 4, ng, n, cscale, active,
-                                wave, lane);
-      if (k + 6 >= ng) break;
-      multi_pair<HD, BS, NW, R>(S, s_b6, s_b7, s_b4, s_b5, a, s_blk, blk0, nblk, kvh, g0, k + 6, ng, n, cscale, active,
-                                wave, lane);
+      multi_quad<HD, BS, NW>(S, s_b4, s_b5, s_b6, s_b7, s_b0, s_b1, s_b2, s_b3, a, s_blk, blk0, nblk, kvh, g0, k + 4,
+                             ng, n, cscale, active, wave, lane);
     }
   } else {
     for (int k = 0; k < ng; k += 4) {
