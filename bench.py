@@ -34,7 +34,7 @@ HBM_PEAK_GBS = 8000.0
 # (profiles/decode_stream_<workload>_hbm_counters.md), valid only for the
 # kernel sources they were taken on.
 PROFILED_TRAFFIC = {
-    "llama3_8b_layer": {"src": "3463aa13cb6eb425", "step_bytes": 577254397, "read_bytes": 576652625},
+    "llama3_8b_layer": {"src": "5702994b158fe2f1", "step_bytes": 577298446, "read_bytes": 576683670},
 }
 KERNEL_SOURCES = ("decode.hip", "pkv_internal.h", "abi.hip")
 
