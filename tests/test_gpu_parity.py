@@ -635,6 +635,24 @@ def test_multi_query_balanced_matches_oracle(rows, H, KV, hd, bs, lo, hi, qlen, 
     check_multi(b, q, part)
 
 
+# Every ring step of the 8-wave query block: rows of 1 .. 12 groups (an
+# exact multiple of 32 positions and a ragged one for each), so that the
+# steps of four groups end at every point -- a lone first group, a pair cut
+# short, refills of one to four groups, and the loop's early exit.  12 rows
+# take the partition path (96 (row, kv head) pairs); 24 rows the balanced
+# one, with slices of one group (pieces everywhere) and with the default.
+@pytest.mark.parametrize("rows,part", [(12, 0), (12, 64), (24, 0), (24, 32)])
+def test_multi_query_ring_steps_at_every_group_count(rows, part):
+    lens = tuple(32 * (1 + i % 12) - (0 if (i // 12) % 2 == 0 else 13) for i in range(rows))
+    note("multi ring steps rows=%d part=%d lens=%s" % (rows, part, lens))
+    cfg = synth.DecodeConfig("multi", "bf16", rows=rows, n_heads=32, n_kv_heads=8, head_dim=128, block_size=16,
+                             ctx=("fixed", lens), pool=("factor", 1.5), max_ctx=max(lens), seed=70 + rows + part)
+    b = synth.make_batch(cfg, device=DEV)
+    g = torch.Generator(device=DEV).manual_seed(71 + rows)
+    q = torch.randn(rows, 64, 32, 128, generator=g, device=DEV).to(torch.bfloat16)
+    check_multi(b, q, part)
+
+
 def test_multi_query_balanced_ignores_poisoned_slots_bitwise():
     cfg = synth.DecodeConfig("multi", "bf16", rows=16, n_heads=32, n_kv_heads=8, head_dim=128, block_size=16,
                              ctx=("uniform", 1, 900), pool=("factor", 1.5), max_ctx=900, seed=63)
