@@ -2520,14 +2520,31 @@ decode_multi_stream(DecodeArgs a) {
 }
 
 // Combine the pieces of the (kv head, row)s that the balanced multi-query
-// read cut, 32 lanes per (row, query, head) as in decode_multi_merge: the
-// same plan as the read finds the pieces (slots stream_piece_slot(first, k)).
+// read cut.  One 256-thread workgroup per (kv head, row, chunk of
+// kStreamMergeCols columns), light enough (registers, LDS) that the whole
+// grid is resident at once: the same plan as the read tells it whether its
+// pair was cut and where the pieces lie (slots stream_piece_slot(first, k));
+// a pair the read wrote whole leaves the workgroup nothing to do.  Four
+// pieces at a time, threads 0 .. 63 fetch each piece's m and l of the chunk's
+// columns into LDS while every thread fetches its acc values: wave w holds 8
+// consecutive columns, whose acc rows are contiguous in every piece, and its
+// load v (of head_dim / 32) reads 1 KiB of them, lane i the 16 bytes at
+// (64 v + i) * 16, four hd values of column (256 v + 4 i) / head_dim.  Then
+//   M = max_k m_k;  L = sum_k l_k 2^(m_k - M);  out = sum_k acc_k 2^(m_k - M) / L
+// folded in slice order (the pieces past the first four rescale the running
+// sums by 2^(M_old - M_new)), so the result does not depend on timing.
+constexpr int kStreamMergeCols = 32;
+template <int HD>
 __global__ __launch_bounds__(256) void decode_multi_stream_merge(DecodeArgs a) {
+  constexpr int F4 = HD / 32;  // 16-byte loads per lane per piece (1 KiB per wave each)
+  constexpr int LPC = HD / 4;  // lanes per column in one load
   __shared__ int32_t s_gpre[kWindowRows + 1];
   __shared__ int32_t s_sum[256 / kWave];
+  __shared__ float s_ml[2][4][kStreamMergeCols];  // m and l of four pieces, the chunk's columns
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
-  const int rows = a.rows, Q = a.query_len, HD = a.head_dim, C = a.cols, G = a.group;
+  const int rows = a.rows, Q = a.query_len, C = a.cols, G = a.group;
   const int cap = a.max_blocks_per_row * a.block_size;
+  
   {
     int x = tid < rows ? a.context_lens[tid] : 0;
     x = x < 0 ? 0 : (x > cap ? cap : x);
@@ -2541,48 +2558,111 @@ __global__ __launch_bounds__(256) void decode_multi_stream_merge(DecodeArgs a) {
     if (tid == 0) s_gpre[rows] = s_sum[0] + s_sum[1] + s_sum[2] + s_sum[3];
     __syncthreads();
   }
-  const int sub = tid & 31;
-  const size_t vh = (size_t)blockIdx.x * kMultiMergeTuples + (tid >> 5);  // (row * Q + query) * n_heads + head
-  if (vh >= (size_t)rows * Q * a.n_heads) return;  // a whole 32-lane half
-  const int r = (int)(vh / ((size_t)Q * a.n_heads));
-  const int rem = (int)(vh - (size_t)r * Q * a.n_heads);
-  const int query = rem / a.n_heads, head = rem - query * a.n_heads;
-  const int kvh = head / G;
+  
+  const int nch = (C + kStreamMergeCols - 1) / kStreamMergeCols;
+  const int pair = (int)blockIdx.x / nch, ch = (int)blockIdx.x - pair * nch;  // pair = kv head * rows + row
+  const int kvh = pair / rows, r = pair - kvh * rows;
   const int ngk = s_gpre[rows], g0 = s_gpre[r], ng = s_gpre[r + 1] - g0 - kMultiSegmentCost;
-  if (ng <= 0) return;  // zeros, written by the read
+  if (ng <= 0) return;  // zeros, written by the read (uniform: the whole workgroup)
   const long long ng_all = (long long)a.n_kv_heads * ngk;
   long long waves = ng_all / max(a.cg_min, 1);
   waves = waves < 1 ? 1 : (waves > a.stream_waves ? a.stream_waves : waves);
-  const long long Sg = (long long)kvh * ngk + g0 + kMultiSegmentCost;  // the row's first group of work
+  const long long Sg = (long long)kvh * ngk + g0 + kMultiSegmentCost;  // the pair's first group of work
   const long long first = slice_of(Sg, ng_all, waves);
   const int nparts = (int)(slice_of(Sg + ng - 1, ng_all, waves) - first + 1);
   if (nparts <= 1) return;  // written by the read
+  const int c0 = ch * kStreamMergeCols;
+  const int d = 4 * (lane % LPC);
+  const int cl0 = 8 * wv + lane / LPC;  // chunk column of load 0; load v adds (kWave / LPC) v
   const StreamLayout L = stream_layout(rows, C, HD, a.stream_waves);
-  const int c = query * G + (head - kvh * G);
   const float *parts = a.ws + L.partials;
-  merge_tuple(
-      a, nparts, sub, vh * HD,
-      [&](int j) { return parts[stream_piece_slot(first, j) * L.slot_stride + (size_t)C * HD + c]; },
-      [&](int j) { return parts[stream_piece_slot(first, j) * L.slot_stride + (size_t)C * HD + C + c]; },
-      [&](int j) { return parts + stream_piece_slot(first, j) * L.slot_stride + (size_t)c * HD; });
+  float M[F4], Lsum[F4];
+  f32x4_t O[F4];
+#pragma unroll
+  for (int v = 0; v < F4; ++v) {
+    M[v] = -INFINITY;
+    Lsum[v] = 0.f;
+    O[v] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  }
+  for (int k0 = 0; k0 < nparts; k0 += 4) {
+    if (k0 > 0) __syncthreads();  // every thread is done with the previous four pieces' m and l
+    if (tid < 2 * 4 * kStreamMergeCols / 2) {  // threads 0 .. 127: (piece u, column) m and l
+      const int u = tid / kStreamMergeCols, cc = tid % kStreamMergeCols;
+      const bool own = k0 + u < nparts && c0 + cc < C;
+      const float *sk = parts + stream_piece_slot(first, own ? k0 + u : 0) * L.slot_stride;
+      const int c = own ? c0 + cc : c0;
+      s_ml[0][u][cc] = own ? sk[(size_t)C * HD + c] : -INFINITY;
+      s_ml[1][u][cc] = own ? sk[(size_t)C * HD + C + c] : 0.f;
+    }
+    f32x4_t x[4][F4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const bool own = k0 + u < nparts;
+      const float *sk = parts + stream_piece_slot(first, own ? k0 + u : 0) * L.slot_stride;
+#pragma unroll
+      for (int v = 0; v < F4; ++v) {
+        const int c = min(c0 + cl0 + (kWave / LPC) * v, C - 1);
+        x[u][v] = own ? *reinterpret_cast<const f32x4_t *>(sk + (size_t)c * HD + d) : f32x4_t{0.f, 0.f, 0.f, 0.f};
+      }
+    }
+    __syncthreads();  // m and l published
+#pragma unroll
+    for (int v = 0; v < F4; ++v) {
+      const int cc = cl0 + (kWave / LPC) * v;
+      const float m0 = s_ml[0][0][cc], m1 = s_ml[0][1][cc], m2 = s_ml[0][2][cc], m3 = s_ml[0][3][cc];
+      const float Mn = fmaxf(M[v], fmaxf(fmaxf(m0, m1), fmaxf(m2, m3)));
+      if (k0 > 0 && Mn != M[v]) {  // the running sums move to the new maximum
+        const float al = exp2_fast(M[v] - Mn);  // M[v] = -inf: nothing accumulated yet, al = 0
+        Lsum[v] *= al;
+        O[v] *= al;
+      }
+      M[v] = Mn;
+      const float mk[4] = {m0, m1, m2, m3};
+#pragma unroll
+      for (int u = 0; u < 4; ++u) {
+        const float w = (mk[u] == -INFINITY) ? 0.f : exp2_fast(mk[u] - Mn);  // Mn = -inf only if every m_k is
+        Lsum[v] = fmaf(s_ml[1][u][cc], w, Lsum[v]);
+        O[v] += w * x[u][v];
+      }
+    }
+  }
+  
+#pragma unroll
+  for (int v = 0; v < F4; ++v) {
+    const int c = c0 + cl0 + (kWave / LPC) * v;
+    if (c >= C) continue;
+    const float inv = Lsum[v] > 0.f ? 1.f / Lsum[v] : 0.f;  // 0: a query before the history
+    const int query = c / G, hi = c - query * G;
+    const size_t o = (((size_t)r * Q + query) * a.n_heads + kvh * G + hi) * HD + d;
+    const float y0 = O[v][0] * inv, y1 = O[v][1] * inv, y2 = O[v][2] * inv, y3 = O[v][3] * inv;
+    if (a.out_dtype == kF32) {
+      *reinterpret_cast<f32x4_t *>(static_cast<float *>(a.out) + o) = f32x4_t{y0, y1, y2, y3};
+    } else {
+      const uint32_t w0 = f32_to_bf16_rne(y0) | ((uint32_t)f32_to_bf16_rne(y1) << 16);
+      const uint32_t w1 = f32_to_bf16_rne(y2) | ((uint32_t)f32_to_bf16_rne(y3) << 16);
+      *reinterpret_cast<uint2 *>(static_cast<uint16_t *>(a.out) + o) = make_uint2(w0, w1);
+    }
+  }
 }
 
 template <int HD, int BS, int NW>
 hipError_t launch_multi_t(const DecodeArgs &a, hipStream_t stream) {
-  const size_t tuples = (size_t)a.rows * a.query_len * a.n_heads;
-  const dim3 merge_grid((unsigned)((tuples + kMultiMergeTuples - 1) / kMultiMergeTuples));
   if (a.stream == 2) {
     hipLaunchKernelGGL((decode_multi_stream<HD, BS, NW>), dim3((unsigned)a.stream_waves), dim3(NW * kWave), 0, stream, a);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
-    hipLaunchKernelGGL(decode_multi_stream_merge, merge_grid, dim3(256), 0, stream, a);
+    const unsigned pairs_chunks =
+        (unsigned)((size_t)a.rows * a.n_kv_heads * ((a.cols + kStreamMergeCols - 1) / kStreamMergeCols));
+    hipLaunchKernelGGL(decode_multi_stream_merge<HD>, dim3(pairs_chunks), dim3(256), 0, stream, a);
     return hipGetLastError();
   }
   const long long units = (long long)a.max_parts * a.q_blocks * a.rows * a.n_kv_heads;
   hipLaunchKernelGGL((decode_multi<HD, BS, NW>), dim3((unsigned)units), dim3(NW * kWave), 0, stream, a);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || a.max_parts <= 1) return e;
-  hipLaunchKernelGGL(decode_multi_merge, merge_grid, dim3(256), 0, stream, a);
+  const size_t tuples = (size_t)a.rows * a.query_len * a.n_heads;
+  hipLaunchKernelGGL(decode_multi_merge, dim3((unsigned)((tuples + kMultiMergeTuples - 1) / kMultiMergeTuples)),
+                     dim3(256), 0, stream, a);
   return hipGetLastError();
 }
 
