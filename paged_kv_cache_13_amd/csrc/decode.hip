@@ -1336,10 +1336,11 @@ __device__ __forceinline__ void segment_end(const DecodeArgs &a, const StreamLay
 // Combine the partials of every (kv head, row) the stream cut into several
 // slices: M = max_k m_k;  L = sum_k l_k 2^(m_k - M);
 // out = sum_k acc_k 2^(m_k - M) / L.  One workgroup per (kv head, row);
-// rows in one slice were written by the stream kernel already.  The maxima
-// are read first (one independent load each), then the weighted sums.
+// rows in one slice were written by the stream kernel already.  Pieces are
+// taken kMergeMaxParts at a time, the running sums moved to each batch's new
+// maximum.  The stream paths have at most 16 columns (a GQA group of at most
+// 16 heads, or a chunk of query_len * group <= 16 columns).
 constexpr int kMergeMaxParts = 8;
-constexpr int kMergeElems = 2;
 __global__ __launch_bounds__(256) void decode_stream_merge(DecodeArgs a) {
   const StreamLayout L = stream_layout(a.rows, a.cols, a.head_dim, a.stream_waves);
   const int32_t *wsi = reinterpret_cast<const int32_t *>(a.ws);
@@ -1389,59 +1390,62 @@ __global__ __launch_bounds__(256) void decode_stream_merge(DecodeArgs a) {
   if (nparts <= 1) return;
   const int C = a.cols, HD = a.head_dim;
   const float *parts = a.ws + L.partials;
-  // Each thread merges kMergeElems outputs at a time, every partial load of
-  // them issued before any output is stored (a store in between would keep
-  // the next loads behind it: the compiler cannot tell out from the
-  // workspace).  Terms are taken in slice order.
-  for (int idx0 = threadIdx.x; idx0 < C * HD; idx0 += kMergeElems * blockDim.x) {
-    float M[kMergeElems], Lm[kMergeElems], O[kMergeElems];
-#pragma unroll
-    for (int e = 0; e < kMergeElems; ++e) M[e] = -INFINITY, Lm[e] = 0.f, O[e] = 0.f;
+  // Each thread merges two adjacent outputs (one column, hd d and d + 1) at a
+  // time: per piece one 8-byte load of their acc values, while threads
+  // 0 .. C * kMergeMaxParts - 1 fetch the pieces' m and l of every column
+  // into LDS.  Every load of a batch of pieces is issued before any output
+  // is stored (a store in between would keep the next loads behind it: the
+  // compiler cannot tell out from the workspace).  Terms are taken in slice
+  // order.  The loop counts are uniform, so the barriers are too.
+  __shared__ float s_ml[2][kMergeMaxParts][16];  // m and l of a batch of pieces, columns < 16
+  const int iters = (C * HD + 2 * (int)blockDim.x - 1) / (2 * (int)blockDim.x);
+  for (int it = 0; it < iters; ++it) {
+    const int idx = 2 * ((int)threadIdx.x + it * (int)blockDim.x);
+    const bool live = idx < C * HD;
+    const int j = live ? idx / HD : 0, d = live ? idx - j * HD : 0;  // HD is even: idx, idx + 1 share column j
+    float M = -INFINITY, Lm = 0.f;
+    f32x2_t O = {0.f, 0.f};
     for (int k0 = 0; k0 < nparts; k0 += kMergeMaxParts) {
       const int kn = min(nparts - k0, kMergeMaxParts);
-      float mk[kMergeElems][kMergeMaxParts], lk[kMergeElems][kMergeMaxParts], ak[kMergeElems][kMergeMaxParts];
+      if (it > 0 || k0 > 0) __syncthreads();  // every thread is done with the previous batch's m and l
+      if ((int)threadIdx.x < C * kMergeMaxParts) {
+        const int u = threadIdx.x / C, jj = threadIdx.x - u * C;
+        const float *sk = parts + stream_piece_slot(first, k0 + min(u, kn - 1)) * L.slot_stride;
+        s_ml[0][u][jj] = u < kn ? sk[C * HD + jj] : -INFINITY;
+        s_ml[1][u][jj] = u < kn ? sk[C * HD + C + jj] : 0.f;
+      }
+      f32x2_t ak[kMergeMaxParts];
 #pragma unroll
-      for (int e = 0; e < kMergeElems; ++e) {
-        const int idx = idx0 + e * blockDim.x;
-        const int j = idx / HD, d = idx - j * HD;
+      for (int k = 0; k < kMergeMaxParts; ++k) {
+        const float *sk = parts + stream_piece_slot(first, k0 + min(k, kn - 1)) * L.slot_stride;
+        ak[k] = k < kn ? *reinterpret_cast<const f32x2_t *>(sk + j * HD + d) : f32x2_t{0.f, 0.f};
+      }
+      __syncthreads();  // m and l published
+      float mn = M;
 #pragma unroll
-        for (int k = 0; k < kMergeMaxParts; ++k) {
-          if (idx < C * HD && k < kn) {
-            const float *sk = parts + stream_piece_slot(first, k0 + k) * L.slot_stride;
-            mk[e][k] = sk[C * HD + j];
-            lk[e][k] = sk[C * HD + C + j];
-            ak[e][k] = sk[j * HD + d];
-          }
+      for (int k = 0; k < kMergeMaxParts; ++k)
+        if (k < kn) mn = fmaxf(mn, s_ml[0][k][j]);
+      const float a0 = M == -INFINITY ? 0.f : exp2_fast(M - mn);
+      Lm *= a0;
+      O[0] *= a0;
+      O[1] *= a0;
+#pragma unroll
+      for (int k = 0; k < kMergeMaxParts; ++k) {
+        if (k < kn) {
+          // a slice that saw nothing of this column (m = -inf) adds nothing
+          const float mk = s_ml[0][k][j];
+          const float wk = mk == -INFINITY ? 0.f : exp2_fast(mk - mn);
+          Lm = fmaf(s_ml[1][k][j], wk, Lm);
+          O[0] = fmaf(ak[k][0], wk, O[0]);
+          O[1] = fmaf(ak[k][1], wk, O[1]);
         }
       }
-#pragma unroll
-      for (int e = 0; e < kMergeElems; ++e) {
-        float mn = M[e];
-#pragma unroll
-        for (int k = 0; k < kMergeMaxParts; ++k)
-          if (k < kn) mn = fmaxf(mn, mk[e][k]);
-        const float a0 = M[e] == -INFINITY ? 0.f : exp2_fast(M[e] - mn);
-        Lm[e] *= a0;
-        O[e] *= a0;
-#pragma unroll
-        for (int k = 0; k < kMergeMaxParts; ++k) {
-          if (k < kn) {
-            // a slice that saw nothing of this column (m = -inf) adds nothing
-            const float wk = mk[e][k] == -INFINITY ? 0.f : exp2_fast(mk[e][k] - mn);
-            Lm[e] = fmaf(lk[e][k], wk, Lm[e]);
-            O[e] = fmaf(ak[e][k], wk, O[e]);
-          }
-        }
-        M[e] = mn;
-      }
+      M = mn;
     }
-#pragma unroll
-    for (int e = 0; e < kMergeElems; ++e) {
-      const int idx = idx0 + e * blockDim.x;
-      if (idx < C * HD) {
-        const int j = idx / HD, d = idx - j * HD;
-        store_out(a.out, a.out_dtype, stream_out_row(a, kvh, r, j) * HD + d, Lm[e] > 0.f ? O[e] / Lm[e] : 0.f);
-      }
+    if (live) {
+      const size_t o = stream_out_row(a, kvh, r, j) * HD + d;
+      store_out(a.out, a.out_dtype, o, Lm > 0.f ? O[0] / Lm : 0.f);
+      store_out(a.out, a.out_dtype, o + 1, Lm > 0.f ? O[1] / Lm : 0.f);
     }
   }
 }
