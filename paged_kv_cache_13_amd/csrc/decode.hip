@@ -1797,17 +1797,14 @@ __device__ __forceinline__ size_t group_block(int j, int32_t id0, int32_t id1, i
 
 // Stage one group: this wave's share of the NSLOT 1 KB slots.  K and V slots
 // are contiguous runs of rows of the K and V tiles (see kswz, vswz32).
-// Positions past `last` read position `last`.
+// Positions past `last` read position `last`.  id0 .. id3 are the block ids
+// of the group's (up to four) blocks.
 template <int HD, int BS, int NW>
-__device__ __forceinline__ void stage_multi(uint4 *st, const DecodeArgs &a, const int32_t *s_blk, int blk0, int nblk,
-                                            int kvh, int t0, int last, int wave, int lane) {
+__device__ __forceinline__ void stage_multi_ids(uint4 *st, const DecodeArgs &a, int32_t id0, int32_t id1, int32_t id2,
+                                                int32_t id3, int kvh, int t0, int last, int wave, int lane) {
   constexpr int KS = HD / 16, NSLOT = HD / 8, SPW = NSLOT / NW, CPR = HD / 8, RPS = 64 / CPR;
   constexpr int LOG2_BS = BS == 8 ? 3 : (BS == 16 ? 4 : 5);
   constexpr int bmask = BS - 1;
-  // the group's (up to four) block ids, the same for every lane
-  const int gb = (t0 >> LOG2_BS) - blk0;
-  int32_t id0, id1, id2, id3;
-  lds_read4(s_blk, gb, min(gb + 1, nblk - 1), min(gb + 2, nblk - 1), min(gb + 3, nblk - 1), id0, id1, id2, id3);
   const int tb0 = t0 >> LOG2_BS;
 #pragma unroll
   for (int x = 0; x < SPW; ++x) {
@@ -1824,6 +1821,70 @@ __device__ __forceinline__ void stage_multi(uint4 *st, const DecodeArgs &a, cons
   }
 }
 
+// The same, reading the group's block ids from s_blk (entries from block
+// blk0 on, nblk of them) first.
+template <int HD, int BS, int NW>
+__device__ __forceinline__ void stage_multi(uint4 *st, const DecodeArgs &a, const int32_t *s_blk, int blk0, int nblk,
+                                            int kvh, int t0, int last, int wave, int lane) {
+  constexpr int LOG2_BS = BS == 8 ? 3 : (BS == 16 ? 4 : 5);
+  const int gb = (t0 >> LOG2_BS) - blk0;
+  int32_t id0, id1, id2, id3;
+  lds_read4(s_blk, gb, min(gb + 1, nblk - 1), min(gb + 2, nblk - 1), min(gb + 3, nblk - 1), id0, id1, id2, id3);
+  stage_multi_ids<HD, BS, NW>(st, a, id0, id1, id2, id3, kvh, t0, last, wave, lane);
+}
+
+// Entries i0 .. i0 + N - 1 of an LDS int table (N = 4, 8 or 16), read in
+// pairs and waited for in one asm block, like lds_read4.  The table must
+// hold N - 1 entries past any i0 this is called with.
+typedef int32_t i32x2_t __attribute__((ext_vector_type(2)));
+template <int N>
+__device__ __forceinline__ void lds_read_run(const int32_t *table, int i0, int32_t (&x)[N]) {
+  static_assert(N == 4 || N == 8 || N == 16, "four groups of 32 positions in blocks of 32, 16 or 8");
+  const uint32_t a0 = (uint32_t)(uintptr_t)((const __attribute__((address_space(3))) int32_t *)table + i0);
+  i32x2_t v[N / 2];
+  if constexpr (N == 4) {
+    asm volatile(
+        "ds_read2_b32 %0, %2 offset0:0 offset1:1\n\t"
+        "ds_read2_b32 %1, %2 offset0:2 offset1:3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1])
+        : "v"(a0)
+        : "memory");
+  } else if constexpr (N == 8) {
+    asm volatile(
+        "ds_read2_b32 %0, %4 offset0:0 offset1:1\n\t"
+        "ds_read2_b32 %1, %4 offset0:2 offset1:3\n\t"
+        "ds_read2_b32 %2, %4 offset0:4 offset1:5\n\t"
+        "ds_read2_b32 %3, %4 offset0:6 offset1:7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3])
+        : "v"(a0)
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read2_b32 %0, %8 offset0:0 offset1:1\n\t"
+        "ds_read2_b32 %1, %8 offset0:2 offset1:3\n\t"
+        "ds_read2_b32 %2, %8 offset0:4 offset1:5\n\t"
+        "ds_read2_b32 %3, %8 offset0:6 offset1:7\n\t"
+        "ds_read2_b32 %4, %8 offset0:8 offset1:9\n\t"
+        "ds_read2_b32 %5, %8 offset0:10 offset1:11\n\t"
+        "ds_read2_b32 %6, %8 offset0:12 offset1:13\n\t"
+        "ds_read2_b32 %7, %8 offset0:14 offset1:15\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(v[0]), "=&v"(v[1]), "=&v"(v[2]), "=&v"(v[3]), "=&v"(v[4]), "=&v"(v[5]), "=&v"(v[6]), "=&v"(v[7])
+        : "v"(a0)
+        : "memory");
+  }
+#pragma unroll
+  for (int i = 0; i < N / 2; ++i) {
+    x[2 * i] = v[i][0];
+    x[2 * i + 1] = v[i][1];
+  }
+}
+
+// Block-id table entries past the last a segment can use: four groups' ids
+// are read in one run from the first group's, whichever of them exist.
+constexpr int kMultiBlkPad = 16;
 
 // Per-wave state of the multi-query read: this lane's column and its
 // softmax state.  acc[dt] register j is output hd 32 dt + 8 (j / 4) +
@@ -1955,10 +2016,22 @@ __device__ __forceinline__ void multi_quad(MultiState<HD> &S, const uint4 *c0, c
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
   uint4 *const r[4] = {r0, r1, r2, r3};
+  if (k + 4 < ng) {
+    // the four groups' block ids in one LDS round trip: IPG per group, from
+    // the first group's first (entries of groups past the last are unused)
+    constexpr int IPG = kGroupPositions / BS;
+    constexpr int LOG2_BS = BS == 8 ? 3 : (BS == 16 ? 4 : 5);
+    const int t4 = (g0 + k + 4) * kGroupPositions;
+    int32_t ids[4 * IPG];
+    lds_read_run<4 * IPG>(s_blk, (t4 >> LOG2_BS) - blk0, ids);
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (k + 4 + i < ng)
-      stage_multi<HD, BS, NW>(r[i], a, s_blk, blk0, nblk, kvh, (g0 + k + 4 + i) * kGroupPositions, n - 1, wave, lane);
+    for (int i = 0; i < 4; ++i)
+      if (k + 4 + i < ng) {
+        const int j = IPG * i;
+        stage_multi_ids<HD, BS, NW>(r[i], a, ids[j], ids[min(j + 1, 4 * IPG - 1)], ids[min(j + 2, 4 * IPG - 1)],
+                                    ids[min(j + 3, 4 * IPG - 1)], kvh, t4 + i * kGroupPositions, n - 1, wave, lane);
+      }
+  }
   if (!active) return;
   multi_pair_compute<HD>(S, c0, c1, a, g0, k, ng, n, cscale, lane);
   if (k + 2 < ng) multi_pair_compute<HD>(S, c2, c3, a, g0, k + 2, ng, n, cscale, lane);
@@ -2148,7 +2221,7 @@ decode_multi(DecodeArgs a) {
   constexpr int LOG2_BS = BS == 8 ? 3 : (BS == 16 ? 4 : 5);
   __shared__ uint4 s_b0[STAGE], s_b1[STAGE], s_b2[STAGE], s_b3[STAGE];
   __shared__ uint4 s_b4[R > 4 ? STAGE : 1], s_b5[R > 4 ? STAGE : 1], s_b6[R > 4 ? STAGE : 1], s_b7[R > 4 ? STAGE : 1];
-  __shared__ int32_t s_blk[kMultiMaxPartition / 8];
+  __shared__ int32_t s_blk[kMultiMaxPartition / 8 + kMultiBlkPad];
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);  // wave-uniform, kept in a scalar
   const int lane = threadIdx.x & (kWave - 1), lr = lane & 31, h = lane >> 5;
   const int G = a.group, Q = a.query_len, QB = a.q_per_tile, P = a.partition_tokens;
@@ -2372,7 +2445,7 @@ decode_multi_stream(DecodeArgs a) {
   constexpr int kSegGroups = kMultiMaxPartition / kGroupPositions;
   __shared__ uint4 s_b0[STAGE], s_b1[STAGE], s_b2[STAGE], s_b3[STAGE];
   __shared__ uint4 s_b4[R > 4 ? STAGE : 1], s_b5[R > 4 ? STAGE : 1], s_b6[R > 4 ? STAGE : 1], s_b7[R > 4 ? STAGE : 1];
-  __shared__ int32_t s_blk[kMultiMaxPartition / 8];
+  __shared__ int32_t s_blk[kMultiMaxPartition / 8 + kMultiBlkPad];
   __shared__ int32_t s_ctx[kWindowRows], s_gpre[kWindowRows + 1];
   __shared__ int32_t s_sum[NW];
   const int tid = threadIdx.x;
