@@ -1886,6 +1886,53 @@ __device__ __forceinline__ void lds_read_run(const int32_t *table, int i0, int32
 // are read in one run from the first group's, whichever of them exist.
 constexpr int kMultiBlkPad = 16;
 
+// Per-lane parts of a group's staging addresses for one (kv head, row):
+// for this wave's slot x, the byte address of its lane's 16 bytes in block
+// 0 of the pool (`base`), and which of the group's blocks holds its
+// position (`j`).  For a group that lies wholly before the row's end, the
+// load address is then base + block id x the pool's block stride.
+template <int HD, int NW>
+struct MultiStageLane {
+  uint64_t base[HD / 8 / NW];
+  int j[HD / 8 / NW];
+};
+
+template <int HD, int BS, int NW>
+__device__ __forceinline__ MultiStageLane<HD, NW> multi_stage_lane(const DecodeArgs &a, int kvh, int wave, int lane) {
+  constexpr int KS = HD / 16, SPW = HD / 8 / NW, CPR = HD / 8, RPS = 64 / CPR;
+  constexpr int LOG2_BS = BS == 8 ? 3 : (BS == 16 ? 4 : 5);
+  MultiStageLane<HD, NW> L;
+#pragma unroll
+  for (int x = 0; x < SPW; ++x) {
+    const int s = wave + NW * x;
+    const bool is_k = s < KS;
+    const int p = RPS * (is_k ? s : s - KS) + lane / CPR;
+    const int col = (lane % CPR) ^ (is_k ? kswz<HD>(p) : vswz32<HD>(p));
+    L.base[x] = (uint64_t)(uintptr_t)(is_k ? a.k_pool : a.v_pool) +
+                ((((uint64_t)kvh << LOG2_BS) + (uint64_t)(p & (BS - 1))) * HD + 8 * col) * 2;
+    L.j[x] = p >> LOG2_BS;
+  }
+  return L;
+}
+
+// stage_multi_ids for a group wholly before the row's end (no position is
+// clamped), from the per-lane parts.
+template <int HD, int BS, int NW>
+__device__ __forceinline__ void stage_multi_fast(uint4 *st, const DecodeArgs &a, const MultiStageLane<HD, NW> &L,
+                                                 int32_t id0, int32_t id1, int32_t id2, int32_t id3, int wave) {
+  constexpr int SPW = HD / 8 / NW;
+  const uint32_t stride = (uint32_t)a.n_kv_heads * (uint32_t)(BS * HD * 2);  // bytes per pool block
+#pragma unroll
+  for (int x = 0; x < SPW; ++x) {
+    const int s = wave + NW * x;
+    const uint32_t bk = (uint32_t)group_block<BS>(L.j[x], id0, id1, id2, id3);
+    const char *src = (const char *)(uintptr_t)(L.base[x] + (uint64_t)bk * stride);
+    __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1))) *)src,
+                                     (void __attribute__((address_space(3))) *)(st + s * kWave), 16, 0,
+                                     kMultiLoadPolicy);
+  }
+}
+
 // Per-wave state of the multi-query read: this lane's column and its
 // softmax state.  acc[dt] register j is output hd 32 dt + 8 (j / 4) +
 // 4 (lane / 32) + j % 4 of the column.
@@ -2010,7 +2057,7 @@ __device__ __forceinline__ void multi_quad(MultiState<HD> &S, const uint4 *c0, c
                                            const uint4 *c3, uint4 *r0, uint4 *r1, uint4 *r2, uint4 *r3,
                                            const DecodeArgs &a, const int32_t *s_blk, int blk0, int nblk, int kvh,
                                            int g0, int k, int ng, int n, float cscale, bool active, int wave,
-                                           int lane) {
+                                           int lane, const MultiStageLane<HD, NW> &SL) {
   __builtin_amdgcn_s_waitcnt(vmcnt_lgkm0(0));
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
@@ -2027,9 +2074,11 @@ __device__ __forceinline__ void multi_quad(MultiState<HD> &S, const uint4 *c0, c
 #pragma unroll
     for (int i = 0; i < 4; ++i)
       if (k + 4 + i < ng) {
-        const int j = IPG * i;
-        stage_multi_ids<HD, BS, NW>(r[i], a, ids[j], ids[min(j + 1, 4 * IPG - 1)], ids[min(j + 2, 4 * IPG - 1)],
-                                    ids[min(j + 3, 4 * IPG - 1)], kvh, t4 + i * kGroupPositions, n - 1, wave, lane);
+        const int j = IPG * i, t0 = t4 + i * kGroupPositions;
+        const int32_t i0 = ids[j], i1 = ids[min(j + 1, 4 * IPG - 1)], i2 = ids[min(j + 2, 4 * IPG - 1)],
+                      i3 = ids[min(j + 3, 4 * IPG - 1)];
+        if (t0 + kGroupPositions <= n) stage_multi_fast<HD, BS, NW>(r[i], a, SL, i0, i1, i2, i3, wave);
+        else stage_multi_ids<HD, BS, NW>(r[i], a, i0, i1, i2, i3, kvh, t0, n - 1, wave, lane);
       }
   }
   if (!active) return;
@@ -2193,12 +2242,13 @@ __device__ __forceinline__ void multi_run(MultiState<HD> &S, uint4 *s_b0, uint4 
   if constexpr (R == 8) {
     stage(s_b2, 2);
     stage(s_b3, 3);
+    const MultiStageLane<HD, NW> SL = multi_stage_lane<HD, BS, NW>(a, kvh, wave, lane);
     for (int k = 0; k < ng; k += 8) {
       multi_quad<HD, BS, NW>(S, s_b0, s_b1, s_b2, s_b3, s_b4, s_b5, s_b6, s_b7, a, s_blk, blk0, nblk, kvh, g0, k, ng,
-                             n, cscale, active, wave, lane);
+                             n, cscale, active, wave, lane, SL);
       if (k + 4 >= ng) break;
       multi_quad<HD, BS, NW>(S, s_b4, s_b5, s_b6, s_b7, s_b0, s_b1, s_b2, s_b3, a, s_blk, blk0, nblk, kvh, g0, k + 4,
-                             ng, n, cscale, active, wave, lane);
+                             ng, n, cscale, active, wave, lane, SL);
     }
   } else {
     for (int k = 0; k < ng; k += 4) {
