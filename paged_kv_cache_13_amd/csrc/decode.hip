@@ -425,52 +425,77 @@ __global__ __launch_bounds__(kThreads) void decode_partition(DecodeArgs a) {
 // Merge of the partitions of rows that span more than one:
 //   M = max_p m_p;  L = sum_p l_p 2^(m_p - M);  out = sum_p acc_p 2^(m_p - M) / L
 // (m_p in the log2 domain).  Rows with one partition were written directly.
+// One workgroup per (row, head), one output per thread (head_dim <= 128).
 // The partials of up to kMergeBatch partitions are loaded together (one
-// round trip per batch, not one per partition), then folded in order.
+// round trip per batch, not one per partition), then folded in order.  The
+// first batch is loaded beside the row's length, before the partition count
+// is known: slots below max_parts lie in the workspace whatever the length,
+// and the slots past the row's last partition (which may hold anything)
+// are then replaced by empty partials.
 constexpr int kMergeBatch = 8;
 __global__ __launch_bounds__(128) void decode_merge(DecodeArgs a) {
   const int r = blockIdx.x / a.n_heads;
   const int h = blockIdx.x % a.n_heads;
   const int cap = a.max_blocks_per_row * a.block_size;
-  int n = a.context_lens[r];
-  n = n < 0 ? 0 : (n > cap ? cap : n);
+  const int n_raw = a.context_lens[r];
   const int P = a.partition_tokens;
-  const int nparts = (n + P - 1) / P;
-  if (nparts <= 1) return;
   const WsLayout ws = ws_layout(a.rows, a.n_heads, a.max_parts, a.head_dim);
   const size_t base = ((size_t)r * a.n_heads + h) * a.max_parts;
   const float *mp = a.ws + ws.m_off + base;
   const float *lp = a.ws + ws.l_off + base;
   const float *ap = a.ws + ws.acc_off + base * a.head_dim;
-  for (int d0 = 0; d0 < a.head_dim; d0 += blockDim.x) {
-    const int d = d0 + (int)threadIdx.x;
-    const bool live = d < a.head_dim;
-    float M = -INFINITY, L = 0.f, O = 0.f;
-    for (int p0 = 0; p0 < nparts; p0 += kMergeBatch) {
-      float mk[kMergeBatch], lk[kMergeBatch], ak[kMergeBatch];
+  const int d = (int)threadIdx.x;
+  const bool live = d < a.head_dim;
+  const int dl = live ? d : 0;
+  const int kl = min(kMergeBatch, a.max_parts) - 1;  // the last slot every row has
+  float mk[kMergeBatch], lk[kMergeBatch], ak[kMergeBatch];
+#pragma unroll
+  for (int k = 0; k < kMergeBatch; ++k) {
+    const int sk = min(k, kl);
+    mk[k] = mp[sk];
+    lk[k] = lp[sk];
+    ak[k] = ap[(size_t)sk * a.head_dim + dl];
+  }
+  // keep these loads ahead of the test below (in flight with the length's)
+#pragma unroll
+  for (int k = 0; k < kMergeBatch; ++k) asm volatile("" ::"v"(mk[k]), "v"(lk[k]), "v"(ak[k]));
+  const int n = n_raw < 0 ? 0 : (n_raw > cap ? cap : n_raw);
+  const int nparts = (n + P - 1) / P;
+  if (nparts <= 1) return;
+  float M = -INFINITY, L = 0.f, O = 0.f;
+  for (int p0 = 0; p0 < nparts; p0 += kMergeBatch) {
+    if (p0 == 0) {
+#pragma unroll
+      for (int k = 0; k < kMergeBatch; ++k)
+        if (k >= nparts) {
+          mk[k] = -INFINITY;
+          lk[k] = 0.f;
+          ak[k] = 0.f;
+        }
+    } else {
 #pragma unroll
       for (int k = 0; k < kMergeBatch; ++k) {
         const bool in = p0 + k < nparts;
         mk[k] = in ? mp[p0 + k] : -INFINITY;
         lk[k] = in ? lp[p0 + k] : 0.f;
-        ak[k] = in && live ? ap[(size_t)(p0 + k) * a.head_dim + d] : 0.f;
+        ak[k] = in ? ap[(size_t)(p0 + k) * a.head_dim + dl] : 0.f;
       }
-      float mn = M;
-#pragma unroll
-      for (int k = 0; k < kMergeBatch; ++k) mn = fmaxf(mn, mk[k]);
-      const float a0 = M == -INFINITY ? 0.f : exp2_fast(M - mn);
-      L *= a0;
-      O *= a0;
-#pragma unroll
-      for (int k = 0; k < kMergeBatch; ++k) {
-        const float wk = mk[k] == -INFINITY ? 0.f : exp2_fast(mk[k] - mn);
-        L = fmaf(lk[k], wk, L);
-        O = fmaf(ak[k], wk, O);
-      }
-      M = mn;
     }
-    if (live) store_out(a.out, a.out_dtype, ((size_t)r * a.n_heads + h) * a.head_dim + d, O / L);
+    float mn = M;
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) mn = fmaxf(mn, mk[k]);
+    const float a0 = M == -INFINITY ? 0.f : exp2_fast(M - mn);
+    L *= a0;
+    O *= a0;
+#pragma unroll
+    for (int k = 0; k < kMergeBatch; ++k) {
+      const float wk = mk[k] == -INFINITY ? 0.f : exp2_fast(mk[k] - mn);
+      L = fmaf(lk[k], wk, L);
+      O = fmaf(ak[k], wk, O);
+    }
+    M = mn;
   }
+  if (live) store_out(a.out, a.out_dtype, ((size_t)r * a.n_heads + h) * a.head_dim + d, O / L);
 }
 
 // ---------------------------------------------------------------------------
