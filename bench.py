@@ -34,7 +34,7 @@ HBM_PEAK_GBS = 8000.0
 # (profiles/decode_stream_<workload>_hbm_counters.md), valid only for the
 # kernel sources they were taken on.
 PROFILED_TRAFFIC = {
-    "llama3_8b_layer": {"src": "01c9d4b8de4902f7", "step_bytes": 577228140, "read_bytes": 576599903},
+    "llama3_8b_layer": {"src": "397b8efc058c85e1", "step_bytes": 577262720, "read_bytes": 576641116},
 }
 KERNEL_SOURCES = ("decode.hip", "pkv_internal.h", "abi.hip")
 
