@@ -275,6 +275,30 @@ def test_read_ignores_poisoned_slots_bitwise(dtype, width):
     assert torch.equal(a, d)
 
 
+@pytest.mark.parametrize("dtype,hd,part", [("f32", 64, 128), ("bf16", 128, 256)])
+def test_partition_merge_ignores_stale_workspace_bitwise(dtype, hd, part):
+    # The partition merge loads its first batch of partial slots beside the
+    # row's length, before it knows how many partitions the row has; slots
+    # past a row's last partition hold whatever an earlier call left (here
+    # NaN everywhere) and must not change a bit of the output.
+    cfg = small_cfg(dtype, rows=6, H=8, KV=2, hd=hd, bs=16, lo=1, hi=1200, seed=22)
+    b = synth.make_batch(cfg, device=DEV)
+    parts = (b.ctx_host + part - 1) // part  # f32: 8 4 7 2 9 1, bf16: 4 2 4 1 5 1
+    assert parts.min() <= 1 and parts.max() > 2, parts  # one-partition rows and split rows
+    nbytes = pkv.workspace_size(b.q, b.k_pool, b.block_table, partition_tokens=part)
+    assert nbytes > 0
+    outs = []
+    for fill in (0x00, 0xFF):  # 0xFF bytes read as NaN floats
+        ws = torch.full((nbytes,), fill, dtype=torch.uint8, device=DEV)
+        out = torch.full(b.q.shape, float("nan"), dtype=torch.float32, device=DEV)
+        pkv.paged_attention_into(b.q, b.k_pool, b.v_pool, b.block_table, b.context_lens, b.scale, out, ws,
+                                 partition_tokens=part)
+        torch.cuda.synchronize()
+        outs.append(out)
+    assert torch.isfinite(outs[1]).all()
+    assert torch.equal(outs[0], outs[1])
+
+
 # ---------------------------------------------------------------------------
 # decode-run sweep: scatter + paged read per step vs the gathered rectangle
 # ---------------------------------------------------------------------------
